@@ -1,0 +1,203 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X (gfx950) paged-KV decode library.
+ *
+ * The problem, as the pages state it: each sequence's logical token
+ * positions live in fixed-size physical blocks named by a block table;
+ * position p of a sequence sits in physical block table[p / B] at offset
+ * p % B, i.e. flat slot table[p / B] * B + p % B ("vLLM PagedAttention: from
+ * fragmentation to slot mapping", section 3). Decode attention over those
+ * blocks must equal softmax(q K^T / sqrt(D)) V over the contiguous history
+ * (same page, section 7; the paper-notes page's block-wise formula and its
+ * 10-token example). New tokens' K/V are written to the slots named by a
+ * slot mapping (same page, section 6, "slot mapping / attention metadata").
+ *
+ * Layouts (all row-major, contiguous, device memory unless stated):
+ *   query          [num_seqs, num_heads, head_size]            dtype
+ *   k_cache/v_cache[num_blocks, num_kv_heads, block_size, head_size] dtype
+ *                  (the glossary page "PagedAttention", teaching layout)
+ *   block_table    [num_seqs, max_blocks_per_seq] int32; entries at and
+ *                  beyond ceil(ctx / block_size) may hold anything (-1 by
+ *                  convention; glossary page, block-table tensor) and are
+ *                  never read
+ *   context_lens   [num_seqs] int32: positions 0..ctx-1 are attended
+ *   slot_mapping   [num_tokens] int64: flat slot, or < 0 for "no write"
+ *   out            [num_seqs, num_heads, head_size] float32
+ * Query head h reads KV head h / (num_heads / num_kv_heads): consecutive
+ * query heads share a KV head (glossary page, expand_kv's repeat_interleave).
+ *
+ * dtype is one of PKV_F32, PKV_F16, PKV_BF16 and applies to query, caches and
+ * new K/V alike. Arithmetic is float32 throughout (scores, softmax, sums).
+ *
+ * Ownership and threading: the caller allocates and owns every buffer. The
+ * library allocates nothing, keeps no pointer after a call returns, has no
+ * mutable global state (calls are reentrant) and never synchronises: each
+ * call validates its arguments on the host, then enqueues kernels on
+ * `stream` (a hipStream_t passed as void*; NULL is the default stream) and
+ * returns. Device faults surface at the caller's next synchronisation.
+ *
+ * Errors: every call returns PKV_OK (0) or a negative pkv_status. All
+ * argument checks run before any HIP call, so a failing call has enqueued
+ * nothing. Values inside device buffers (block ids, lengths, slots) cannot be
+ * checked on the host; the kernels never dereference a block id outside
+ * [0, num_blocks) or a table entry outside the row (such positions are
+ * skipped), so a bad value gives a wrong answer, not a fault.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  PKV_ERR_DTYPE = -3,       /* unknown dtype code */
+  PKV_ERR_UNSUPPORTED = -4, /* valid, but no kernel handles this shape */
+  PKV_ERR_WORKSPACE = -5,   /* split requested without its workspace */
+  PKV_ERR_LAUNCH = -6       /* the HIP runtime refused a launch */
+};
+
+/*
+ * paged_slot_mapping -- flat slot of each sequence's new token.
+ *
+ * slot_mapping[s] = block_table[s][p / B] * B + p % B with p = positions[s]
+ * ("vLLM PagedAttention ...", section 3; the source-walkthrough page
+ * "vLLM source walkthrough: PagedAttention and continuous batching",
+ * section 1.7). A negative position, a position whose logical block is at or
+ * beyond max_blocks_per_seq, or a negative table entry gives -1.
+ *
+ * slot_mapping: [num_seqs] int64, written. block_table: [num_seqs,
+ * max_blocks_per_seq] int32. positions: [num_seqs] int32.
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE (num_seqs < 0, max_blocks_per_seq < 1,
+ * block_size < 1). num_seqs == 0 is a no-op.
+ */
+int paged_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                       const int32_t* positions, int num_seqs, int max_blocks_per_seq,
+                       int block_size, void* stream);
+
+/*
+ * paged_kv_write -- store new tokens' K and V at their slots.
+ *
+ * For each i with 0 <= s = slot_mapping[i] < num_blocks * block_size and
+ * every kv head h: k_cache[s / B][h][s % B][:] = k_new[i][h][:], likewise V.
+ * A bit copy (the backend "writes new K/V to physical slots": "vLLM
+ * PagedAttention ...", section 6). Other slots are untouched.
+ *
+ * k_new/v_new: [num_tokens, num_kv_heads, head_size] dtype.
+ * Preconditions (not checkable on the host): non-negative slots are
+ * distinct, and each target block is owned by one sequence. Shared full
+ * blocks are read-only and each sequence writes only into its own last
+ * block (nxmr.cn article, sections 4.2-4.3); copy-on-write is the caller's.
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE. num_tokens == 0 is a
+ * no-op.
+ */
+int paged_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                   const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                   int num_kv_heads, int block_size, int head_size, int dtype,
+                   void* stream);
+
+/*
+ * paged_decode_attention -- one query token per sequence over its paged KV.
+ *
+ * For sequence s and query head h (KV head kv = h / (num_heads/num_kv_heads)),
+ * with z_t = scale * <q[s][h], K_s[kv][t]> over positions t < ctx_s:
+ *   out[s][h] = sum_t exp(z_t - max z) V_s[kv][t] / sum_t exp(z_t - max z),
+ * where K_s[kv][t] = k_cache[block_table[s][t / B]][kv][t % B]
+ * ("vLLM PagedAttention ...", sections 3 and 7; paper-notes page, block-wise
+ * formula). scale is normally 1/sqrt(head_size).
+ *
+ * partition_size == 0: `out` is written directly; the workspace pointers may
+ * be NULL and max_partitions is ignored.
+ * partition_size > 0 (a multiple of block_size): the context is split into
+ * partitions of partition_size positions computed in parallel (the
+ * source-walkthrough page, section 1.8, "V2" partitions followed by a reduce
+ * kernel). For p < ceil(ctx_s / partition_size) the call writes
+ *   max_logits[s][h][p] = m_p  = max of z_t over the partition,
+ *   exp_sums[s][h][p]   = l_p  = sum exp(z_t - m_p),
+ *   tmp_out[s][h][p][:] = o_p  = sum exp(z_t - m_p) V[t] / l_p,
+ * leaves other partition slots and `out` untouched, and the caller then calls
+ * paged_attention_reduce. Workspace layouts: max_logits and exp_sums
+ * [num_seqs, num_heads, max_partitions] float32, tmp_out [num_seqs,
+ * num_heads, max_partitions, head_size] float32; see
+ * paged_attention_workspace_bytes.
+ *
+ * ctx_s == 0 gives out = 0. Preconditions: ctx_s <= max_blocks_per_seq * B
+ * (longer contexts are cut there), and in split mode ctx_s <= max_partitions *
+ * partition_size (later partitions are not computed).
+ *
+ * Supported: f32/f16/bf16; head_size 1..256; any block_size >= 1; any
+ * num_heads / num_kv_heads ratio. The fast path (matrix-core scores,
+ * LDS-free lane broadcasts) covers f16/bf16, head_size 128, block_size a
+ * multiple of 16 and groups of up to 16 query heads per KV head; other
+ * shapes run a plain wave-per-head kernel.
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE (num_heads % num_kv_heads != 0, sizes
+ * < 1, partition_size not a positive multiple of block_size, max_partitions
+ * < 1 in split mode), PKV_ERR_DTYPE, PKV_ERR_UNSUPPORTED (head_size > 256),
+ * PKV_ERR_WORKSPACE (split mode with a NULL workspace pointer),
+ * PKV_ERR_LAUNCH. num_seqs == 0 is a no-op.
+ */
+int paged_decode_attention(float* out, const void* query, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* context_lens, int num_seqs, int num_heads,
+                           int num_kv_heads, int head_size, int block_size,
+                           int64_t num_blocks, int max_blocks_per_seq, float scale,
+                           int partition_size, int max_partitions, float* max_logits,
+                           float* exp_sums, float* tmp_out, int dtype, void* stream);
+
+/*
+ * paged_attention_reduce -- merge split partials into the final output.
+ *
+ * For each (s, h) with n = ceil(ctx_s / partition_size) partitions (n is
+ * clamped to max_partitions), M = max_p m_p and w_p = l_p * exp(m_p - M):
+ *   out[s][h][:] = sum_p w_p o_p / sum_p w_p,   out = 0 when n == 0.
+ * The pages name only "a reduce kernel that merges the partitions"
+ * (source-walkthrough page, section 1.8); this is the exact log-sum-exp merge
+ * of the partials paged_decode_attention writes. Partition slots p >= n are
+ * never read. Layouts as in paged_decode_attention.
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_LAUNCH. num_seqs == 0 is a
+ * no-op.
+ */
+int paged_attention_reduce(float* out, const float* max_logits, const float* exp_sums,
+                           const float* tmp_out, const int32_t* context_lens, int num_seqs,
+                           int num_heads, int head_size, int partition_size,
+                           int max_partitions, void* stream);
+
+/*
+ * paged_attention_workspace_bytes -- bytes of max_logits + exp_sums + tmp_out
+ * for a split call: num_seqs * num_heads * max_partitions * (head_size + 2) *
+ * 4. Host-only; returns 0 for non-positive arguments.
+ */
+size_t paged_attention_workspace_bytes(int num_seqs, int num_heads, int head_size,
+                                       int max_partitions);
+
+/*
+ * paged_kv_gather -- contiguous copy of each sequence's K and V (for checks).
+ *
+ * k_out[s][h][t][:] = k_cache[block_table[s][t / B]][h][t % B][:] for
+ * t < min(ctx_s, max_ctx), likewise V; rows t >= ctx_s are left untouched.
+ * This is the glossary page's gather_paged (paged -> contiguous), run through
+ * the same device translation helper as the attention kernels, so that a
+ * bytewise comparison checks block-table translation exactly.
+ * k_out/v_out: [num_seqs, num_kv_heads, max_ctx, head_size] dtype.
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_LAUNCH.
+ */
+int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                    const int32_t* block_table, const int32_t* context_lens, int num_seqs,
+                    int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
+                    int max_blocks_per_seq, int max_ctx, int dtype, void* stream);
+
+/* pkv_strerror -- static description of a pkv_status code. */
+const char* pkv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,144 @@
+"""Python binding of libpagedkv.so, the gfx950 paged-KV decode library.
+
+Argument marshalling only: each function takes torch tensors, passes their
+device pointers, sizes and torch's current HIP stream to the C entry point of
+the same name (include/pagedkv.h) and raises on a non-zero status. Every step
+of the computation runs in the library's HIP kernels; there is no fallback.
+If the library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+_DTYPE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+
+# C signatures, mirrored from include/pagedkv.h
+_P, _I32, _I64, _F32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+SIGNATURES = {
+    "paged_slot_mapping": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P]),
+    "paged_kv_write": (_I32, [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P]),
+    "paged_decode_attention": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                      _I64, _I32, _F32, _I32, _I32, _P, _P, _P, _I32, _P]),
+    "paged_attention_reduce": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
+    "paged_attention_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
+    "paged_kv_gather": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32,
+                               _I32, _I32, _P]),
+    "pkv_strerror": (ctypes.c_char_p, [_I32]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python __graft_entry__.py` "
+            "(hipcc --offload-arch=gfx950); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed: {code} ({lib.pkv_strerror(code).decode()})")
+        self.code = code
+
+
+def _check(fn, code):
+    if code != 0:
+        raise PagedKVError(fn, code)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def paged_slot_mapping(slot_mapping, block_table, positions, block_size, stream=None):
+    """slot_mapping[s] = block_table[s][p // B] * B + p % B, p = positions[s]."""
+    _dev(slot_mapping, block_table, positions)
+    assert slot_mapping.dtype == torch.int64 and block_table.dtype == torch.int32
+    assert positions.dtype == torch.int32
+    _check("paged_slot_mapping", lib.paged_slot_mapping(
+        _ptr(slot_mapping), _ptr(block_table), _ptr(positions), positions.shape[0],
+        block_table.shape[1], block_size, _stream(stream)))
+
+
+def paged_kv_write(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
+    """Store k_new/v_new [T, Hkv, D] at their slots of [N, Hkv, B, D] pools."""
+    _dev(k_cache, v_cache, k_new, v_new, slot_mapping)
+    assert k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype
+    assert slot_mapping.dtype == torch.int64
+    n, hkv, b, d = k_cache.shape
+    _check("paged_kv_write", lib.paged_kv_write(
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+        k_new.shape[0], n, hkv, b, d, _DTYPE[k_cache.dtype], _stream(stream)))
+
+
+def paged_decode_attention(out, query, k_cache, v_cache, block_table, context_lens, scale,
+                           partition_size=0, max_partitions=0, max_logits=None,
+                           exp_sums=None, tmp_out=None, stream=None):
+    """Decode attention; split mode writes the partials (see include/pagedkv.h)."""
+    _dev(out, query, k_cache, v_cache, block_table, context_lens, max_logits, exp_sums,
+         tmp_out)
+    assert block_table.dtype == torch.int32 and context_lens.dtype == torch.int32
+    assert out is None or out.dtype == torch.float32
+    n, hkv, b, d = k_cache.shape
+    s, hq, _ = query.shape
+    _check("paged_decode_attention", lib.paged_decode_attention(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(context_lens), s, hq, hkv, d, b, n, block_table.shape[1], float(scale),
+        partition_size, max_partitions, _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out),
+        _DTYPE[query.dtype], _stream(stream)))
+
+
+def paged_attention_reduce(out, max_logits, exp_sums, tmp_out, context_lens, partition_size,
+                           stream=None):
+    """Log-sum-exp merge of split partials [S, Hq, P(, D)] into out [S, Hq, D]."""
+    _dev(out, max_logits, exp_sums, tmp_out, context_lens)
+    s, hq, p, d = tmp_out.shape
+    _check("paged_attention_reduce", lib.paged_attention_reduce(
+        _ptr(out), _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out), _ptr(context_lens), s, hq,
+        d, partition_size, p, _stream(stream)))
+
+
+def paged_attention_workspace_bytes(num_seqs, num_heads, head_size, max_partitions):
+    return int(lib.paged_attention_workspace_bytes(num_seqs, num_heads, head_size,
+                                                   max_partitions))
+
+
+def paged_kv_gather(k_out, v_out, k_cache, v_cache, block_table, context_lens, stream=None):
+    """Contiguous copy [S, Hkv, max_ctx, D] of each sequence's K and V."""
+    _dev(k_out, v_out, k_cache, v_cache, block_table, context_lens)
+    n, hkv, b, d = k_cache.shape
+    s, _, max_ctx, _ = k_out.shape
+    _check("paged_kv_gather", lib.paged_kv_gather(
+        _ptr(k_out), _ptr(v_out), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(context_lens), s, hkv, d, b, n, block_table.shape[1], max_ctx,
+        _DTYPE[k_cache.dtype], _stream(stream)))
+
+
+def pkv_strerror(code):
+    return lib.pkv_strerror(code).decode()

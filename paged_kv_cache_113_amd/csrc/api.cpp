@@ -1,0 +1,162 @@
+// C ABI of the paged-KV library: host-side argument validation, kernel
+// choice and launch on the caller's stream. Every check runs before any HIP
+// call, so invalid calls enqueue nothing and are testable without a GPU.
+#include <hip/hip_runtime.h>
+
+#include "../../include/pagedkv.h"
+#include "launch.h"
+
+namespace {
+
+int elem_bytes(int dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    default: return 0;
+  }
+}
+
+constexpr int kMaxGridYZ = 65535;
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int paged_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                       const int32_t* positions, int num_seqs, int max_blocks_per_seq,
+                       int block_size, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq < 1 || block_size < 1) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!slot_mapping || !block_table || !positions) return PKV_ERR_NULL;
+  return launch_status(pkv::launch_slot_mapping(slot_mapping, block_table, positions, num_seqs,
+                                                max_blocks_per_seq, block_size,
+                                                as_stream(stream)));
+}
+
+int paged_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                   const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                   int num_kv_heads, int block_size, int head_size, int dtype, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return PKV_ERR_DTYPE;
+  if (num_tokens < 0 || num_blocks < 1 || num_kv_heads < 1 || block_size < 1 || head_size < 1)
+    return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return PKV_ERR_NULL;
+  // the grid is one thread per 2-byte chunk at worst
+  const int64_t chunks = num_tokens * num_kv_heads * (static_cast<int64_t>(head_size) * eb / 2);
+  if (chunks / 256 >= 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  return launch_status(pkv::launch_kv_write(k_cache, v_cache, k_new, v_new, slot_mapping,
+                                            num_tokens, num_blocks, num_kv_heads, block_size,
+                                            head_size, eb, as_stream(stream)));
+}
+
+int paged_decode_attention(float* out, const void* query, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* context_lens, int num_seqs, int num_heads,
+                           int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
+                           int max_blocks_per_seq, float scale, int partition_size,
+                           int max_partitions, float* max_logits, float* exp_sums,
+                           float* tmp_out, int dtype, void* stream) {
+  if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_size < 1 || block_size < 1 ||
+      num_blocks < 1 || max_blocks_per_seq < 1 || partition_size < 0)
+    return PKV_ERR_SHAPE;
+  if (num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  const bool split = partition_size > 0;
+  if (split && (partition_size % block_size != 0 || max_partitions < 1)) return PKV_ERR_SHAPE;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > 0x7fffffff) return PKV_ERR_SHAPE;
+  if (head_size > 256) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!query || !k_cache || !v_cache || !block_table || !context_lens) return PKV_ERR_NULL;
+  if (!split && !out) return PKV_ERR_NULL;
+  if (split && (!max_logits || !exp_sums || !tmp_out)) return PKV_ERR_WORKSPACE;
+
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.query = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = head_size;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.scale = scale;
+  a.partition_size = partition_size;
+  a.max_partitions = split ? max_partitions : 1;
+  a.max_logits = max_logits;
+  a.exp_sums = exp_sums;
+  a.tmp_out = tmp_out;
+  a.dtype = dtype;
+  if (pkv::fast_decode_supported(a))
+    return launch_status(pkv::launch_decode_fast(a, as_stream(stream)));
+  if (num_seqs > kMaxGridYZ || num_heads > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  return launch_status(pkv::launch_decode_generic(a, as_stream(stream)));
+}
+
+int paged_attention_reduce(float* out, const float* max_logits, const float* exp_sums,
+                           const float* tmp_out, const int32_t* context_lens, int num_seqs,
+                           int num_heads, int head_size, int partition_size, int max_partitions,
+                           void* stream) {
+  if (num_seqs < 0 || num_heads < 1 || head_size < 1 || partition_size < 1 ||
+      max_partitions < 1)
+    return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !max_logits || !exp_sums || !tmp_out || !context_lens) return PKV_ERR_NULL;
+  if (num_seqs > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  return launch_status(pkv::launch_reduce(out, max_logits, exp_sums, tmp_out, context_lens,
+                                          num_seqs, num_heads, head_size, partition_size,
+                                          max_partitions, as_stream(stream)));
+}
+
+size_t paged_attention_workspace_bytes(int num_seqs, int num_heads, int head_size,
+                                       int max_partitions) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_size <= 0 || max_partitions <= 0) return 0;
+  return static_cast<size_t>(num_seqs) * num_heads * max_partitions * (head_size + 2) *
+         sizeof(float);
+}
+
+int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                    const int32_t* block_table, const int32_t* context_lens, int num_seqs,
+                    int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
+                    int max_blocks_per_seq, int max_ctx, int dtype, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_kv_heads < 1 || head_size < 1 || block_size < 1 || num_blocks < 1 ||
+      max_blocks_per_seq < 1 || max_ctx < 0)
+    return PKV_ERR_SHAPE;
+  if (num_seqs == 0 || max_ctx == 0) return PKV_OK;
+  if (!k_out || !v_out || !k_cache || !v_cache || !block_table || !context_lens)
+    return PKV_ERR_NULL;
+  const int64_t chunks = static_cast<int64_t>(num_seqs) * num_kv_heads * max_ctx *
+                         (static_cast<int64_t>(head_size) * eb / 2);
+  if (chunks / 256 >= 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  return launch_status(pkv::launch_kv_gather(k_out, v_out, k_cache, v_cache, block_table,
+                                             context_lens, num_seqs, num_kv_heads, head_size,
+                                             block_size, num_blocks, max_blocks_per_seq, max_ctx,
+                                             eb, as_stream(stream)));
+}
+
+const char* pkv_strerror(int code) {
+  switch (code) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case PKV_ERR_DTYPE: return "unknown dtype code";
+    case PKV_ERR_UNSUPPORTED: return "no kernel handles this shape";
+    case PKV_ERR_WORKSPACE: return "split mode needs max_logits, exp_sums and tmp_out";
+    case PKV_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    default: return "unknown pkv status code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Paged decode attention, plain path: any dtype (f32/f16/bf16), head size up
+// to 256, any block size and head grouping. One wave per (sequence, query
+// head, partition); positions are visited one at a time through the block
+// table (block = p / B, offset = p % B: "vLLM PagedAttention: from
+// fragmentation to slot mapping", section 3) with an online softmax. It is
+// the path for the small and unusual shapes; the matrix-core kernel covers
+// the 128-wide heads that carry the bandwidth.
+//
+// Also the split-partial merge: out = sum_p l_p e^{m_p - M} o_p /
+// sum_p l_p e^{m_p - M} (the merge of the source-walkthrough page's V2
+// partitions, section 1.8; the pages do not print its formula).
+#include "device.h"
+#include "launch.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kMaxPerLane = 4;  // head_size <= 256
+
+template <typename T>
+__global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x;
+  const int part = blockIdx.x;
+  const int h = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int G = a.num_heads / a.num_kv_heads;
+  const int kvh = h / G;
+  const int D = a.head_size;
+  const int B = a.block_size;
+
+  int ctx = a.context_lens[seq];
+  const int cap = a.max_blocks * B;
+  ctx = ctx < cap ? ctx : cap;
+  int lo = 0, hi = ctx;
+  if (a.partition_size > 0) {
+    lo = part * a.partition_size;
+    if (lo >= ctx) return;
+    hi = lo + a.partition_size < ctx ? lo + a.partition_size : ctx;
+  }
+  const T* __restrict__ q = static_cast<const T*>(a.query) +
+                            (static_cast<int64_t>(seq) * a.num_heads + h) * D;
+  const T* __restrict__ kc = static_cast<const T*>(a.k_cache);
+  const T* __restrict__ vc = static_cast<const T*>(a.v_cache);
+  const int32_t* __restrict__ row = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
+
+  float qv[kMaxPerLane], acc[kMaxPerLane];
+#pragma unroll
+  for (int k = 0; k < kMaxPerLane; ++k) {
+    const int d = lane + 64 * k;
+    qv[k] = d < D ? to_float(q[d]) : 0.f;
+    acc[k] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int t = lo; t < hi; ++t) {
+    const int64_t blk = physical_block(row, t, B, a.max_blocks, a.num_blocks);
+    if (blk < 0) continue;  // a table entry outside the pool: skipped
+    const int64_t base = pool_row(blk, kvh, t % B, a.num_kv_heads, B, D);
+    float dot = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxPerLane; ++k) {
+      const int d = lane + 64 * k;
+      if (d < D) dot = fmaf(qv[k], to_float(kc[base + d]), dot);
+    }
+    const float z = wave_sum(dot) * a.scale;
+    const float m_new = fmaxf(m, z);
+    const float alpha = expf(m - m_new);  // 0 on the first position
+    const float p = expf(z - m_new);
+    l = l * alpha + p;
+#pragma unroll
+    for (int k = 0; k < kMaxPerLane; ++k) {
+      const int d = lane + 64 * k;
+      const float v = d < D ? to_float(vc[base + d]) : 0.f;
+      acc[k] = fmaf(p, v, acc[k] * alpha);
+    }
+    m = m_new;
+  }
+  const int64_t orow = static_cast<int64_t>(seq) * a.num_heads + h;
+  if (a.partition_size > 0) {
+    const int64_t pidx = orow * a.max_partitions + part;
+#pragma unroll
+    for (int k = 0; k < kMaxPerLane; ++k) {
+      const int d = lane + 64 * k;
+      if (d < D) a.tmp_out[pidx * D + d] = l > 0.f ? acc[k] / l : 0.f;
+    }
+    if (lane == 0) {
+      a.max_logits[pidx] = m;
+      a.exp_sums[pidx] = l;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kMaxPerLane; ++k) {
+      const int d = lane + 64 * k;
+      if (d < D) a.out[orow * D + d] = l > 0.f ? acc[k] / l : 0.f;
+    }
+  }
+}
+
+// One wave per (sequence, head): lanes own dims d = lane + 64k.
+__global__ __launch_bounds__(64) void reduce_kernel(float* __restrict__ out,
+                                                    const float* __restrict__ max_logits,
+                                                    const float* __restrict__ exp_sums,
+                                                    const float* __restrict__ tmp_out,
+                                                    const int32_t* __restrict__ context_lens,
+                                                    int num_heads, int head_size,
+                                                    int partition_size, int max_partitions) {
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int D = head_size;
+  const int64_t orow = static_cast<int64_t>(seq) * num_heads + h;
+  const int ctx = context_lens[seq];
+  int n = ctx > 0 ? (ctx + partition_size - 1) / partition_size : 0;
+  n = n < max_partitions ? n : max_partitions;
+  const float* __restrict__ m = max_logits + orow * max_partitions;
+  const float* __restrict__ l = exp_sums + orow * max_partitions;
+  const float* __restrict__ o = tmp_out + orow * max_partitions * D;
+
+  float M = -INFINITY;
+  for (int p = lane; p < n; p += 64) M = fmaxf(M, m[p]);
+  M = wave_max(M);
+  float den = 0.f;
+  for (int p = lane; p < n; p += 64) den += l[p] * expf(m[p] - M);
+  den = wave_sum(den);
+  for (int d0 = 0; d0 < D; d0 += 64) {
+    const int d = d0 + lane;
+    float num = 0.f;
+    for (int p = 0; p < n; ++p) {
+      const float wgt = l[p] * expf(m[p] - M);  // uniform per p
+      if (d < D) num = fmaf(wgt, o[static_cast<int64_t>(p) * D + d], num);
+    }
+    if (d < D) out[orow * D + d] = (n > 0 && den > 0.f) ? num / den : 0.f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream) {
+  dim3 grid(a.partition_size > 0 ? a.max_partitions : 1, a.num_heads, a.num_seqs);
+  dim3 block(64);
+  switch (a.dtype) {
+    case 0: decode_generic_kernel<float><<<grid, block, 0, stream>>>(a); break;
+    case 1: decode_generic_kernel<f16_t><<<grid, block, 0, stream>>>(a); break;
+    default: decode_generic_kernel<bf16_t><<<grid, block, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(float* out, const float* max_logits, const float* exp_sums,
+                         const float* tmp_out, const int32_t* context_lens, int num_seqs,
+                         int num_heads, int head_size, int partition_size, int max_partitions,
+                         hipStream_t stream) {
+  dim3 grid(num_heads, num_seqs);
+  reduce_kernel<<<grid, 64, 0, stream>>>(out, max_logits, exp_sums, tmp_out, context_lens,
+                                         num_heads, head_size, partition_size, max_partitions);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,79 @@
+// Device helpers shared by the gfx950 kernels of the paged-KV library.
+//
+// Block-table translation follows "vLLM PagedAttention: from fragmentation to
+// slot mapping", section 3: position p of a sequence lives in physical block
+// table[p / B] at offset p % B. Pools are [num_blocks, Hkv, B, D].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Storage types. Conversions to float are exact.
+struct bf16_t { uint16_t bits; };
+struct f16_t { uint16_t bits; };
+
+__device__ __forceinline__ float to_float(float x) { return x; }
+__device__ __forceinline__ float to_float(bf16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
+}
+__device__ __forceinline__ float to_float(f16_t x) {
+  _Float16 h;
+  __builtin_memcpy(&h, &x.bits, 2);
+  return static_cast<float>(h);
+}
+
+// The two halves of a 32-bit word holding two 16-bit values, widened.
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float lo_f16(uint32_t w) {
+  _Float16 h;
+  uint16_t b = static_cast<uint16_t>(w);
+  __builtin_memcpy(&h, &b, 2);
+  return static_cast<float>(h);
+}
+__device__ __forceinline__ float hi_f16(uint32_t w) {
+  _Float16 h;
+  uint16_t b = static_cast<uint16_t>(w >> 16);
+  __builtin_memcpy(&h, &b, 2);
+  return static_cast<float>(h);
+}
+
+// Physical block of logical position `pos`, or -1 when the table row does not
+// cover it or holds an id outside [0, num_blocks). Callers skip such
+// positions, so a bad table never turns into an out-of-bounds access.
+__device__ __forceinline__ int64_t physical_block(const int32_t* table_row, int pos,
+                                                  int block_size, int max_blocks,
+                                                  int64_t num_blocks) {
+  int lb = pos / block_size;
+  if (pos < 0 || lb >= max_blocks) return -1;
+  int64_t b = table_row[lb];
+  return (b >= 0 && b < num_blocks) ? b : -1;
+}
+
+// Element offset of pool[block][kv][off][0] in a [num_blocks, Hkv, B, D] pool.
+__device__ __forceinline__ int64_t pool_row(int64_t block, int kv, int off, int num_kv_heads,
+                                            int block_size, int head_size) {
+  return ((block * num_kv_heads + kv) * block_size + off) * static_cast<int64_t>(head_size);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// 2^x on the hardware exponential unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace pkv

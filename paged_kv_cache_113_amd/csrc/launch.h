@@ -1,0 +1,56 @@
+// Host-side launchers of the gfx950 kernels. Arguments are already
+// validated by the C ABI layer (api.cpp); each launcher returns the HIP error
+// of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                               const int32_t* positions, int num_seqs, int max_blocks,
+                               int block_size, hipStream_t stream);
+
+hipError_t launch_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                           int num_kv_heads, int block_size, int head_size, int elem_bytes,
+                           hipStream_t stream);
+
+hipError_t launch_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, const int32_t* context_lens,
+                            int num_seqs, int num_kv_heads, int head_size, int block_size,
+                            int64_t num_blocks, int max_blocks, int max_ctx, int elem_bytes,
+                            hipStream_t stream);
+
+struct DecodeArgs {
+  float* out;
+  const void* query;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int num_seqs, num_heads, num_kv_heads, head_size, block_size;
+  int64_t num_blocks;
+  int max_blocks;
+  float scale;
+  int partition_size;  // 0: unsplit
+  int max_partitions;  // >= 1
+  float* max_logits;
+  float* exp_sums;
+  float* tmp_out;
+  int dtype;           // pkv_dtype
+};
+
+// Matrix-core path: f16/bf16, head_size 128, block_size % 16 == 0, G <= 16.
+bool fast_decode_supported(const DecodeArgs& a);
+hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream);
+// Plain path: every supported shape.
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_reduce(float* out, const float* max_logits, const float* exp_sums,
+                         const float* tmp_out, const int32_t* context_lens, int num_seqs,
+                         int num_heads, int head_size, int partition_size, int max_partitions,
+                         hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,148 @@
+"""The C ABI library loads, exports every entry point include/pagedkv.h
+declares, and rejects bad arguments on the host before any HIP call (so
+these run without a GPU: no call below reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+LIB = os.path.join(ROOT, "paged_kv_cache_113_amd", "libpagedkv.so")
+
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, ELAUNCH = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built (run python __graft_entry__.py)")
+    import paged_kv_cache_113_amd as pkv
+    return pkv.lib
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("paged_kv_write", "paged_decode_attention", "paged_attention_reduce",
+              "paged_slot_mapping", "paged_kv_gather", "paged_attention_workspace_bytes",
+              "pkv_strerror"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    import paged_kv_cache_113_amd as pkv
+    assert set(pkv.SIGNATURES) == set(declared_functions())
+
+
+def test_strerror(lib):
+    for code in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, ELAUNCH):
+        assert len(lib.pkv_strerror(code)) > 0
+    assert b"unknown" in lib.pkv_strerror(12345)
+
+
+def test_workspace_bytes(lib):
+    assert lib.paged_attention_workspace_bytes(8, 64, 128, 256) == 8 * 64 * 256 * 130 * 4
+    assert lib.paged_attention_workspace_bytes(0, 64, 128, 256) == 0
+    assert lib.paged_attention_workspace_bytes(8, 64, 128, -1) == 0
+
+
+P = ctypes.c_void_p(16)   # a non-NULL pointer that is never dereferenced
+
+
+def attn(lib, **kw):
+    a = dict(out=P, q=P, k=P, v=P, table=P, ctx=P, S=2, Hq=8, Hkv=2, D=128, B=16, N=10,
+             MB=4, scale=0.1, psz=0, mp=0, ml=None, es=None, to=None, dtype=2)
+    a.update(kw)
+    return lib.paged_decode_attention(a["out"], a["q"], a["k"], a["v"], a["table"], a["ctx"],
+                                      a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["N"],
+                                      a["MB"], a["scale"], a["psz"], a["mp"], a["ml"], a["es"],
+                                      a["to"], a["dtype"], None)
+
+
+def test_attention_validation(lib):
+    assert attn(lib, dtype=7) == EDTYPE
+    assert attn(lib, Hq=6, Hkv=4) == ESHAPE
+    assert attn(lib, Hq=0) == ESHAPE
+    assert attn(lib, D=0) == ESHAPE
+    assert attn(lib, B=0) == ESHAPE
+    assert attn(lib, N=0) == ESHAPE
+    assert attn(lib, MB=0) == ESHAPE
+    assert attn(lib, S=-1) == ESHAPE
+    assert attn(lib, psz=-16) == ESHAPE
+    assert attn(lib, psz=24) == ESHAPE                 # not a multiple of B
+    assert attn(lib, psz=32, mp=0) == ESHAPE
+    assert attn(lib, D=512) == EUNSUP
+    assert attn(lib, S=0) == OK                          # no-op, nothing launched
+    assert attn(lib, q=None) == ENULL
+    assert attn(lib, table=None) == ENULL
+    assert attn(lib, out=None) == ENULL                  # unsplit needs out
+    assert attn(lib, psz=32, mp=4) == EWS                # split needs the workspace
+    assert attn(lib, psz=32, mp=4, ml=P, es=P) == EWS
+
+
+def test_reduce_validation(lib):
+    f = lib.paged_attention_reduce
+    assert f(P, P, P, P, P, 2, 8, 128, 0, 4, None) == ESHAPE
+    assert f(P, P, P, P, P, 2, 8, 128, 512, 0, None) == ESHAPE
+    assert f(P, P, P, P, P, 2, 0, 128, 512, 4, None) == ESHAPE
+    assert f(None, P, P, P, P, 2, 8, 128, 512, 4, None) == ENULL
+    assert f(P, P, None, P, P, 2, 8, 128, 512, 4, None) == ENULL
+    assert f(P, P, P, P, P, 0, 8, 128, 512, 4, None) == OK
+    assert f(P, P, P, P, P, 70000, 8, 128, 512, 4, None) == EUNSUP
+
+
+def test_write_validation(lib):
+    f = lib.paged_kv_write
+    assert f(P, P, P, P, P, 4, 10, 2, 16, 128, 9, None) == EDTYPE
+    assert f(P, P, P, P, P, -1, 10, 2, 16, 128, 2, None) == ESHAPE
+    assert f(P, P, P, P, P, 4, 0, 2, 16, 128, 2, None) == ESHAPE
+    assert f(P, P, P, P, P, 4, 10, 0, 16, 128, 2, None) == ESHAPE
+    assert f(None, P, P, P, P, 4, 10, 2, 16, 128, 2, None) == ENULL
+    assert f(P, P, P, P, None, 4, 10, 2, 16, 128, 2, None) == ENULL
+    assert f(P, P, P, P, P, 0, 10, 2, 16, 128, 2, None) == OK
+
+
+def test_slot_mapping_and_gather_validation(lib):
+    f = lib.paged_slot_mapping
+    assert f(P, P, P, 4, 0, 16, None) == ESHAPE
+    assert f(P, P, P, 4, 8, 0, None) == ESHAPE
+    assert f(P, P, P, -1, 8, 16, None) == ESHAPE
+    assert f(None, P, P, 4, 8, 16, None) == ENULL
+    assert f(P, P, P, 0, 8, 16, None) == OK
+    g = lib.paged_kv_gather
+    assert g(P, P, P, P, P, P, 2, 2, 128, 16, 10, 4, 64, 5, None) == EDTYPE
+    assert g(P, P, P, P, P, P, 2, 2, 128, 16, 0, 4, 64, 2, None) == ESHAPE
+    assert g(P, P, P, P, P, P, 2, 2, 128, 16, 10, 4, -1, 2, None) == ESHAPE
+    assert g(None, P, P, P, P, P, 2, 2, 128, 16, 10, 4, 64, 2, None) == ENULL
+    assert g(P, P, P, P, P, P, 2, 2, 128, 16, 10, 4, 0, 2, None) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import paged_kv_cache_113_amd as pkv
+    x = torch.zeros(2, 4, 8)
+    with pytest.raises(ValueError):
+        pkv.paged_decode_attention(x, x, x.view(2, 4, 1, 8), x.view(2, 4, 1, 8),
+                                   torch.zeros(2, 1, dtype=torch.int32),
+                                   torch.zeros(2, dtype=torch.int32), 0.5)
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The library package and the input generators never import oracle/."""
+    for sub in ("paged_kv_cache_113_amd", "workloads"):
+        for dirpath, _, files in os.walk(os.path.join(ROOT, sub)):
+            for fn in files:
+                if fn.endswith((".py", ".cpp", ".hip", ".h")):
+                    text = open(os.path.join(dirpath, fn)).read()
+                    assert "import oracle" not in text and "from oracle" not in text, fn
+                    assert "attn_ref" not in text and "liboracle" not in text, fn
