@@ -1,0 +1,300 @@
+"""Benchmark of the paged-KV decode hot path on one MI355X.
+
+Default workload: the full decode step -- 512 sequences, cached lengths
+U{64..4096}, 32 layers, bf16, Hq=32, Hkv=8, D=128, block 16. One step = one
+slot-mapping launch for the batch, then for every layer: the new tokens' K/V
+write, split decode attention (1024-position partitions) and the
+log-sum-exp merge. Inputs are resident in HBM before timing starts.
+
+Prints one JSON line. `value` is KV-read GB/s over the whole step: the
+algorithmic bytes every layer must read (2 * Hkv * D * 2 B per live
+(sequence, position)) divided by the step time. The `roofline` object is for
+the decode kernel alone, timed with HIP events on the stream it runs on.
+The `cpu_baseline` object times the fp64 CPU oracle on a bounded sample of the
+same workload (rank 0, one GPU only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode KV-read HBM GB/s (% of MI355X peak) + decoded seqs·tokens/s"
+HBM_PEAK_GBS = 8000.0
+DECODE_SOURCES = ["paged_kv_cache_113_amd/csrc/decode_fast.hip",
+                  "paged_kv_cache_113_amd/csrc/device.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in DECODE_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str, kernel_bytes_per_launch: float):
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"decode_fast_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def kv_bytes(batch, lens) -> float:
+    e = {"f32": 4, "f16": 2, "bf16": 2}[batch.dtype]
+    return float(np.sum(lens, dtype=np.int64)) * 2 * batch.num_kv_heads * batch.head_size * e
+
+
+def make_batch(workload):
+    import workloads as W
+    return W.CASES[workload]()
+
+
+def default_partition(workload):
+    return {"decode_step_bf16": 1024, "long_split_bf16": 512, "mha_fp16": 0,
+            "gqa_shared_bf16": 0, "tiny": 0}[workload]
+
+
+def cpu_baseline(batch, th, target_s: float, threads: int):
+    """Time the fp64 oracle on layer 0 of the workload (post-write pools made
+    by the oracle's own scatter): all sequences with ``threads`` workers,
+    repeated to about target_s / 2, and one worker on a prefix of a seeded
+    sequence order sized to about target_s / 2."""
+    import oracle
+    k = oracle._raw(th["k_cache"], batch.dtype)
+    v = oracle._raw(th["v_cache"], batch.dtype)
+    if batch.positions is not None:
+        slots = oracle.allocator.slot_mapping(
+            [r[r >= 0].tolist() for r in batch.block_table], batch.positions.tolist(),
+            batch.block_size)
+        k = oracle.scatter.scatter(k, oracle._raw(th["k_new"], batch.dtype), slots)
+        v = oracle.scatter.scatter(v, oracle._raw(th["v_new"], batch.dtype), slots)
+    scale = float(np.float32(1.0 / math.sqrt(batch.head_size)))
+
+    def run(seqs, nthreads):
+        t0 = time.perf_counter()
+        oracle.attention(th["q"], k, v, batch.block_table, batch.context_lens, scale,
+                         batch.dtype, seqs=seqs, threads=nthreads)
+        return time.perf_counter() - t0
+
+    everything = np.arange(batch.num_seqs, dtype=np.int32)
+    reps, spent = 0, 0.0
+    while spent < target_s / 2 or reps == 0:
+        spent += run(everything, threads)
+        reps += 1
+    all_rate = kv_bytes(batch, batch.context_lens) * reps / spent
+    order = np.random.default_rng(7).permutation(batch.num_seqs).astype(np.int32)
+    probe = order[:2]
+    dt = run(probe, 1)
+    per_pos = dt / max(1, int(batch.context_lens[probe].sum()))
+    csum = np.cumsum(batch.context_lens[order])
+    n1 = int(max(1, min(len(order), np.searchsorted(csum, (target_s / 2) / per_pos) + 1)))
+    dt1 = run(order[:n1], 1)
+    one_rate = kv_bytes(batch, batch.context_lens[order[:n1]]) / dt1
+    pos = float(batch.context_lens.sum())
+    return {"value": round(all_rate / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"layer 0 of the workload, all {batch.num_seqs} sequences "
+                      f"({int(pos)} positions) x {reps} repeats in {spent:.1f} s; "
+                      f"fp64 gather + attention",
+            "seq_tokens_per_s": round(pos * reps / spent, 1),
+            "single_thread": {"value": round(one_rate / 1e9, 4), "unit": "GB/s",
+                              "sample": f"{n1} sequences of layer 0, {dt1:.1f} s"}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode_step_bf16",
+                    choices=["decode_step_bf16", "mha_fp16", "gqa_shared_bf16",
+                             "long_split_bf16"])
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None, help="decode step only (default 32)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences and KV heads shard with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_113_amd as pkv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    batch = make_batch(args.workload)
+    if args.layers is not None:
+        batch.num_layers = args.layers
+    L = batch.num_layers
+    P = default_partition(args.workload) if args.partition_size is None else args.partition_size
+    mp = batch.max_partitions(P) if P > 0 else 1
+    scale = float(np.float32(1.0 / math.sqrt(batch.head_size)))
+    print(f"[bench] workload {args.workload}: S={batch.num_seqs} layers={L} "
+          f"blocks/layer={batch.num_blocks} P={P}", file=sys.stderr, flush=True)
+
+    t0 = time.perf_counter()
+    layers = []
+    cpu_host = None
+    for l in range(L):
+        t = W.layer_tensors(batch, layer=l, device=dev)
+        if l == 0 and not args.no_cpu_baseline:
+            cpu_host = {k: v.cpu() for k, v in t.items()}
+        layers.append(t)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+
+    table = torch.as_tensor(batch.block_table, device=dev)
+    ctx = torch.as_tensor(batch.context_lens, device=dev)
+    pos = torch.as_tensor(batch.positions, device=dev) if batch.positions is not None else None
+    slots = torch.empty(batch.num_seqs, dtype=torch.int64, device=dev)
+    outs = [torch.empty(batch.num_seqs, batch.num_heads, batch.head_size, device=dev)
+            for _ in range(L)]
+    if P > 0:
+        ws_shape = (batch.num_seqs, batch.num_heads, mp)
+        ml = torch.empty(ws_shape, device=dev)
+        es = torch.empty(ws_shape, device=dev)
+        to = torch.empty(ws_shape + (batch.head_size,), device=dev)
+    flush = None
+    if args.workload != "decode_step_bf16":
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+
+    ev = {k: [] for k in ("decode", "reduce", "write")}
+
+    def step(record):
+        if pos is not None:
+            pkv.paged_slot_mapping(slots, table, pos, batch.block_size)
+        for l, t in enumerate(layers):
+            if pos is not None:
+                if record:
+                    e0 = torch.cuda.Event(enable_timing=True); e0.record()
+                pkv.paged_kv_write(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], slots)
+                if record:
+                    e1 = torch.cuda.Event(enable_timing=True); e1.record()
+                    ev["write"].append((e0, e1))
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True); e0.record()
+            if P > 0:
+                pkv.paged_decode_attention(None, t["q"], t["k_cache"], t["v_cache"], table, ctx,
+                                           scale, P, mp, ml, es, to)
+            else:
+                pkv.paged_decode_attention(outs[l], t["q"], t["k_cache"], t["v_cache"], table,
+                                           ctx, scale)
+            if record:
+                e1 = torch.cuda.Event(enable_timing=True); e1.record()
+                ev["decode"].append((e0, e1))
+            if P > 0:
+                if record:
+                    e0 = torch.cuda.Event(enable_timing=True); e0.record()
+                pkv.paged_attention_reduce(outs[l], ml, es, to, ctx, P)
+                if record:
+                    e1 = torch.cuda.Event(enable_timing=True); e1.record()
+                    ev["reduce"].append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    if args.copy_probe:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b_ = torch.empty_like(a)
+        for _ in range(5):
+            b_.copy_(a)
+        torch.cuda.synchronize()
+        del a, b_
+
+    step_ms = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    if flush is None:
+        for _ in range(args.steps):
+            step(True)
+        torch.cuda.synchronize()
+        total_s = time.perf_counter() - t_start
+    else:
+        # single-layer workloads: evict L2/MALL before each step (not timed)
+        total_s = 0.0
+        for _ in range(args.steps):
+            flush.fill_(1.0)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            step(True)
+            torch.cuda.synchronize()
+            total_s += time.perf_counter() - t1
+    ms_per_step = total_s / args.steps * 1e3
+
+    def avg_ms(name):
+        xs = [a.elapsed_time(b) for a, b in ev[name]]
+        return (float(np.mean(xs)), float(np.percentile(xs, 10)), float(np.percentile(xs, 90))) \
+            if xs else (0.0, 0.0, 0.0)
+
+    dec_ms, dec_p10, dec_p90 = avg_ms("decode")
+    red_ms = avg_ms("reduce")[0]
+    wr_ms = avg_ms("write")[0]
+    layer_bytes = kv_bytes(batch, batch.context_lens)
+    step_bytes = layer_bytes * L
+    value = step_bytes / (ms_per_step / 1e3) / 1e9
+    achieved = layer_bytes / (dec_ms / 1e3) / 1e9
+    positions = float(np.sum(batch.context_lens, dtype=np.int64))
+    traffic = traffic_for(args.workload, layer_bytes)
+
+    cpu = None
+    if cpu_host is not None:
+        threads = min(os.cpu_count() or 1, 16)
+        print(f"[bench] cpu baseline: oracle, {threads} threads, ~{args.cpu_seconds:.0f} s",
+              file=sys.stderr, flush=True)
+        cpu = cpu_baseline(batch, cpu_host, args.cpu_seconds, threads)
+
+    config = {"workload": args.workload, "num_seqs": batch.num_seqs, "layers": L,
+              "num_heads": batch.num_heads, "num_kv_heads": batch.num_kv_heads,
+              "head_size": batch.head_size, "block_size": batch.block_size,
+              "context_lens": f"{int(batch.context_lens.min())}..{int(batch.context_lens.max())}"
+                              f" mean {float(batch.context_lens.mean()):.1f}",
+              "partition_size": P, "blocks_per_layer": batch.num_blocks}
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": batch.dtype, "data": "synthetic", "config": config,
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seq_tokens_per_s": round(positions * L / (ms_per_step / 1e3), 1),
+        "new_tokens_per_s": round(batch.num_seqs / (ms_per_step / 1e3), 1)
+        if batch.positions is not None else None,
+        "kernels_ms": {"decode_avg": round(dec_ms, 4), "decode_p10": round(dec_p10, 4),
+                       "decode_p90": round(dec_p90, 4), "reduce_avg": round(red_ms, 4),
+                       "write_avg": round(wr_ms, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_fast_kernel",
+                     "bytes_per_launch": layer_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,7 +44,7 @@ namespace {
 
 constexpr int kD = 128;     // head size of this path
 constexpr int kTile = 16;   // positions per tile
-constexpr int kWaves = 4;   // waves per workgroup
+constexpr int kWavesUnsplit = 4;  // waves per (sequence, KV head) without a split
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -127,19 +127,27 @@ __device__ __forceinline__ void load_tile(TileRegs& t, const char* __restrict__ 
     t.v[i] = *reinterpret_cast<const uint4*>(vbase + v_off + i * 256);
 }
 
-template <typename T, int GM>
-__global__ __launch_bounds__(kWaves * 64) void decode_fast_kernel(DecodeArgs a) {
+// NW waves share one (sequence, KV head, partition) item and merge through
+// LDS (NW = 4, used without a split), or each 64-lane workgroup is one item
+// (NW = 1, used with a split: each wave owns a whole partition, so the
+// serial start of an item -- length, table entry, first tile -- is paid once
+// per partition, and no barrier is needed).
+template <typename T, int GM, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_fast_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   // wave index, made visibly uniform so table reads become scalar loads
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;  // K row / score column (head) / V dim chunk
   const int grp = lane >> 4;  // row group j
 
-  const int num_parts = a.partition_size > 0 ? a.max_partitions : 1;
+  // Item order: KV head fastest, then sequence, then partition. Workgroups
+  // that run at the same time then read the KV heads of the same physical
+  // blocks, which sit next to each other in the pool (Hkv * B * D contiguous
+  // elements per block), and every sequence's first partitions go first.
   const int item = blockIdx.x;
-  const int part = item % num_parts;
-  const int kvh = (item / num_parts) % a.num_kv_heads;
-  const int seq = item / (num_parts * a.num_kv_heads);
+  const int kvh = item % a.num_kv_heads;
+  const int seq = (item / a.num_kv_heads) % a.num_seqs;
+  const int part = item / (a.num_kv_heads * a.num_seqs);
   const int G = a.num_heads / a.num_kv_heads;
   const int B = a.block_size;
 
@@ -153,7 +161,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_fast_kernel(DecodeArgs a) 
     hi = lo + a.partition_size < ctx ? lo + a.partition_size : ctx;
   }
   const int n_tiles = (hi - lo + kTile - 1) / kTile;
-  const int my_n = n_tiles > w ? (n_tiles - w + kWaves - 1) / kWaves : 0;
+  const int my_n = n_tiles > w ? (n_tiles - w + NW - 1) / NW : 0;
 
   const int32_t* __restrict__ row = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
   const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_fast_kernel(DecodeArgs a) 
   // Issue the loads of tile ti. Returns false when the table entry is outside
   // the pool: block 0 is loaded instead (in bounds) and the tile is masked.
   auto load = [&](TileRegs& t, int ti) -> bool {
-    const int tok0 = lo + (w + kWaves * ti) * kTile;
+    const int tok0 = lo + (w + NW * ti) * kTile;
     const int64_t blk = physical_block(row, tok0, B, a.max_blocks, a.num_blocks);
     const int64_t base = (blk < 0 ? 0 : blk) * block_stride + kvh * head_stride +
                          static_cast<int64_t>(tok0 % B) * kD * 2;
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_fast_kernel(DecodeArgs a) 
   };
 
   auto process = [&](const TileRegs& t, int ti, bool good) {
-    const int tok0 = lo + (w + kWaves * ti) * kTile;
+    const int tok0 = lo + (w + NW * ti) * kTile;
     const int lim = good ? hi - tok0 : 0;  // rows >= lim are masked
     f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -269,62 +277,92 @@ __global__ __launch_bounds__(kWaves * 64) void decode_fast_kernel(DecodeArgs a) 
     for (int e = 0; e < 8; ++e) acc[n][e] = sum_xor32(sum_xor16(acc[n][e]));
   l_part = sum_xor32(sum_xor16(l_part));
 
-  // merge the waves through LDS
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
-  __shared__ float sm_acc[kWaves][GM][kD];
-  if (grp == 0) {
-    sm_m[w][col] = m_run;
-    sm_l[w][col] = l_part;
-#pragma unroll
-    for (int n = 0; n < GM; ++n)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[w][n][col * 8 + e] = acc[n][e];
-  }
-  __syncthreads();
-
   const int64_t out_row0 = static_cast<int64_t>(seq) * a.num_heads + kvh * G;
-  for (int idx = threadIdx.x; idx < G * kD; idx += kWaves * 64) {
-    const int n = idx / kD;
-    const int d = idx % kD;
-    float M = -INFINITY;
+  if constexpr (NW == 1) {
+    // lane (0, n) holds column n's running max and sum; every lane holds
+    // acc[n][dims 8*col..8*col+7] for all heads n
+    static_for<0, GM>([&](auto nc) {
+      constexpr int n = decltype(nc)::value;
+      if (n < G) {
+        const float ln = row_bcast<n>(l_part);
+        float o[8];
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][n]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float den = 0.f, num = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = fast_exp2(sm_m[ww][n] - Mu);
-      den = fmaf(f, sm_l[ww][n], den);
-      num = fmaf(f, sm_acc[ww][n][d], num);
-    }
-    const float o = den > 0.f ? num / den : 0.f;
-    if (a.partition_size > 0) {
-      const int64_t pidx = (out_row0 + n) * a.max_partitions + part;
-      a.tmp_out[pidx * kD + d] = o;
-      if (d == 0) {
-        a.max_logits[pidx] = M * kLn2;  // back to natural-log units
-        a.exp_sums[pidx] = den;
+        for (int e = 0; e < 8; ++e) o[e] = ln > 0.f ? acc[n][e] / ln : 0.f;
+        float* dst = a.partition_size > 0
+                         ? a.tmp_out + ((out_row0 + n) * a.max_partitions + part) * kD
+                         : a.out + (out_row0 + n) * kD;
+        if (grp == 0) {
+          reinterpret_cast<float4*>(dst + col * 8)[0] = make_float4(o[0], o[1], o[2], o[3]);
+          reinterpret_cast<float4*>(dst + col * 8)[1] = make_float4(o[4], o[5], o[6], o[7]);
+        }
       }
-    } else {
-      a.out[(out_row0 + n) * kD + d] = o;
+    });
+    if (a.partition_size > 0 && grp == 0 && col < G) {
+      const int64_t pidx = (out_row0 + col) * a.max_partitions + part;
+      a.max_logits[pidx] = m_run * kLn2;  // back to natural-log units
+      a.exp_sums[pidx] = l_part;
+    }
+  } else {
+    // merge the waves through LDS
+    __shared__ float sm_m[NW][16];
+    __shared__ float sm_l[NW][16];
+    __shared__ float sm_acc[NW][GM][kD];
+    if (grp == 0) {
+      sm_m[w][col] = m_run;
+      sm_l[w][col] = l_part;
+#pragma unroll
+      for (int n = 0; n < GM; ++n)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm_acc[w][n][col * 8 + e] = acc[n][e];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * kD; idx += NW * 64) {
+      const int n = idx / kD;
+      const int d = idx % kD;
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][n]);
+      const float Mu = M == -INFINITY ? 0.f : M;
+      float den = 0.f, num = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float f = fast_exp2(sm_m[ww][n] - Mu);
+        den = fmaf(f, sm_l[ww][n], den);
+        num = fmaf(f, sm_acc[ww][n][d], num);
+      }
+      const float o = den > 0.f ? num / den : 0.f;
+      if (a.partition_size > 0) {
+        const int64_t pidx = (out_row0 + n) * a.max_partitions + part;
+        a.tmp_out[pidx * kD + d] = o;
+        if (d == 0) {
+          a.max_logits[pidx] = M * kLn2;  // back to natural-log units
+          a.exp_sums[pidx] = den;
+        }
+      } else {
+        a.out[(out_row0 + n) * kD + d] = o;
+      }
     }
   }
 }
 
-template <typename T>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+template <typename T, int NW>
+hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
   const int G = a.num_heads / a.num_kv_heads;
   const int parts = a.partition_size > 0 ? a.max_partitions : 1;
   const int64_t items = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * parts;
   dim3 grid(static_cast<unsigned>(items));
-  dim3 block(kWaves * 64);
-  if (G <= 1) decode_fast_kernel<T, 1><<<grid, block, 0, stream>>>(a);
-  else if (G <= 2) decode_fast_kernel<T, 2><<<grid, block, 0, stream>>>(a);
-  else if (G <= 4) decode_fast_kernel<T, 4><<<grid, block, 0, stream>>>(a);
-  else if (G <= 8) decode_fast_kernel<T, 8><<<grid, block, 0, stream>>>(a);
-  else decode_fast_kernel<T, 16><<<grid, block, 0, stream>>>(a);
+  dim3 block(NW * 64);
+  if (G <= 1) decode_fast_kernel<T, 1, NW><<<grid, block, 0, stream>>>(a);
+  else if (G <= 2) decode_fast_kernel<T, 2, NW><<<grid, block, 0, stream>>>(a);
+  else if (G <= 4) decode_fast_kernel<T, 4, NW><<<grid, block, 0, stream>>>(a);
+  else if (G <= 8) decode_fast_kernel<T, 8, NW><<<grid, block, 0, stream>>>(a);
+  else decode_fast_kernel<T, 16, NW><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  return a.partition_size > 0 ? launch_nw<T, 1>(a, stream) : launch_nw<T, kWavesUnsplit>(a, stream);
 }
 
 }  // namespace

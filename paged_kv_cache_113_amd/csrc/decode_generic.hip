@@ -95,15 +95,25 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
   }
 }
 
-// One wave per (sequence, head): lanes own dims d = lane + 64k.
-__global__ __launch_bounds__(64) void reduce_kernel(float* __restrict__ out,
-                                                    const float* __restrict__ max_logits,
-                                                    const float* __restrict__ exp_sums,
-                                                    const float* __restrict__ tmp_out,
-                                                    const int32_t* __restrict__ context_lens,
-                                                    int num_heads, int head_size,
-                                                    int partition_size, int max_partitions) {
-  const int lane = threadIdx.x;
+// Merge of split partials: one 256-thread workgroup per (sequence, head).
+// The weights w_p = l_p e^{m_p - M} are computed once per partition (all
+// threads in parallel) and staged in LDS in chunks; each wave then
+// accumulates every 4th partition over all dims (lane owns dims lane + 64k,
+// coalesced 4-byte rows), and the four waves' sums meet in LDS.
+constexpr int kRedThreads = 256;
+constexpr int kRedChunk = 2048;
+
+__global__ __launch_bounds__(kRedThreads) void reduce_kernel(
+    float* __restrict__ out, const float* __restrict__ max_logits,
+    const float* __restrict__ exp_sums, const float* __restrict__ tmp_out,
+    const int32_t* __restrict__ context_lens, int num_heads, int head_size, int partition_size,
+    int max_partitions) {
+  __shared__ float s_w[kRedChunk];
+  __shared__ float s_red[kRedThreads / 64];
+  __shared__ float s_acc[kRedThreads / 64][kMaxPerLane * 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int D = head_size;
@@ -115,20 +125,51 @@ __global__ __launch_bounds__(64) void reduce_kernel(float* __restrict__ out,
   const float* __restrict__ l = exp_sums + orow * max_partitions;
   const float* __restrict__ o = tmp_out + orow * max_partitions * D;
 
-  float M = -INFINITY;
-  for (int p = lane; p < n; p += 64) M = fmaxf(M, m[p]);
-  M = wave_max(M);
+  float mx = -INFINITY;
+  for (int p = tid; p < n; p += kRedThreads) mx = fmaxf(mx, m[p]);
+  mx = wave_max(mx);
+  if (lane == 0) s_red[w] = mx;
+  __syncthreads();
+  float M = s_red[0];
+#pragma unroll
+  for (int i = 1; i < kRedThreads / 64; ++i) M = fmaxf(M, s_red[i]);
+
+  float acc[kMaxPerLane] = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int p = lane; p < n; p += 64) den += l[p] * expf(m[p] - M);
-  den = wave_sum(den);
-  for (int d0 = 0; d0 < D; d0 += 64) {
-    const int d = d0 + lane;
-    float num = 0.f;
-    for (int p = 0; p < n; ++p) {
-      const float wgt = l[p] * expf(m[p] - M);  // uniform per p
-      if (d < D) num = fmaf(wgt, o[static_cast<int64_t>(p) * D + d], num);
+  for (int c0 = 0; c0 < n; c0 += kRedChunk) {
+    const int cn = n - c0 < kRedChunk ? n - c0 : kRedChunk;
+    __syncthreads();  // previous chunk's weights are no longer read
+    for (int p = tid; p < cn; p += kRedThreads) {
+      const float wp = l[c0 + p] * expf(m[c0 + p] - M);
+      s_w[p] = wp;
+      den += wp;
     }
-    if (d < D) out[orow * D + d] = (n > 0 && den > 0.f) ? num / den : 0.f;
+    __syncthreads();
+#pragma unroll 4
+    for (int p = w; p < cn; p += kRedThreads / 64) {
+      const float wp = s_w[p];
+      const float* __restrict__ row = o + static_cast<int64_t>(c0 + p) * D;
+#pragma unroll
+      for (int k = 0; k < kMaxPerLane; ++k) {
+        const int d = lane + 64 * k;
+        if (d < D) acc[k] = fmaf(wp, row[d], acc[k]);
+      }
+    }
+  }
+  den = wave_sum(den);
+  __syncthreads();
+  if (lane == 0) s_red[w] = den;
+#pragma unroll
+  for (int k = 0; k < kMaxPerLane; ++k) s_acc[w][lane + 64 * k] = acc[k];
+  __syncthreads();
+  float total = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRedThreads / 64; ++i) total += s_red[i];
+  for (int d = tid; d < D; d += kRedThreads) {
+    float num = 0.f;
+#pragma unroll
+    for (int i = 0; i < kRedThreads / 64; ++i) num += s_acc[i][d];
+    out[orow * D + d] = (n > 0 && total > 0.f) ? num / total : 0.f;
   }
 }
 
@@ -150,7 +191,7 @@ hipError_t launch_reduce(float* out, const float* max_logits, const float* exp_s
                          int num_heads, int head_size, int partition_size, int max_partitions,
                          hipStream_t stream) {
   dim3 grid(num_heads, num_seqs);
-  reduce_kernel<<<grid, 64, 0, stream>>>(out, max_logits, exp_sums, tmp_out, context_lens,
+  reduce_kernel<<<grid, kRedThreads, 0, stream>>>(out, max_logits, exp_sums, tmp_out, context_lens,
                                          num_heads, head_size, partition_size, max_partitions);
   return hipGetLastError();
 }
