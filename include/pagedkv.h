@@ -115,28 +115,34 @@ int paged_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* 
  *
  * partition_size == 0: `out` is written directly; the workspace pointers may
  * be NULL and max_partitions is ignored.
- * partition_size > 0 (a multiple of block_size): the context is split into
- * partitions of partition_size positions computed in parallel (the
- * source-walkthrough page, section 1.8, "V2" partitions followed by a reduce
- * kernel). For p < ceil(ctx_s / partition_size) the call writes
- *   max_logits[s][h][p] = m_p  = max of z_t over the partition,
- *   exp_sums[s][h][p]   = l_p  = sum exp(z_t - m_p),
+ * partition_size > 0 (a multiple of block_size): split mode, the "V2"
+ * scheme of the source-walkthrough page, section 1.8 (a sequence's context is
+ * cut into pieces computed in parallel, then merged by a reduce kernel). The
+ * library cuts every sequence into at most max_partitions pieces of
+ * consecutive positions, balancing the pieces over the whole GPU; the caller
+ * sizes max_partitions >= ceil(max ctx / partition_size). For each (s, h)
+ * with ctx_s >= 1 and each slot p < max_partitions the call writes either a
+ * piece's partial
+ *   max_logits[s][h][p] = m_p  = max of z_t over the piece,
+ *   exp_sums[s][h][p]   = l_p  = sum exp(z_t - m_p)   (>= 1),
  *   tmp_out[s][h][p][:] = o_p  = sum exp(z_t - m_p) V[t] / l_p,
- * leaves other partition slots and `out` untouched, and the caller then calls
- * paged_attention_reduce. Workspace layouts: max_logits and exp_sums
- * [num_seqs, num_heads, max_partitions] float32, tmp_out [num_seqs,
+ * or marks the slot unused (l_p = 0, m_p = -inf). `out` is untouched; the
+ * caller then calls paged_attention_reduce. Workspace layouts: max_logits and
+ * exp_sums [num_seqs, num_heads, max_partitions] float32, tmp_out [num_seqs,
  * num_heads, max_partitions, head_size] float32; see
- * paged_attention_workspace_bytes.
+ * paged_attention_workspace_bytes. (The plain kernel cuts exactly at
+ * multiples of partition_size.)
  *
  * ctx_s == 0 gives out = 0. Preconditions: ctx_s <= max_blocks_per_seq * B
  * (longer contexts are cut there), and in split mode ctx_s <= max_partitions *
- * partition_size (later partitions are not computed).
+ * partition_size (with the plain kernel, later partitions are not computed).
  *
  * Supported: f32/f16/bf16; head_size 1..256; any block_size >= 1; any
- * num_heads / num_kv_heads ratio. The fast path (matrix-core scores,
- * LDS-free lane broadcasts) covers f16/bf16, head_size 128, block_size a
- * multiple of 16 and groups of up to 16 query heads per KV head; other
- * shapes run a plain wave-per-head kernel.
+ * num_heads / num_kv_heads ratio. The fast path (matrix-core scores, DPP
+ * lane broadcasts, balanced persistent split) covers f16/bf16, head_size
+ * 128, block_size a multiple of 16, groups of up to 16 query heads per KV
+ * head and, in split mode, up to 8192 sequences; other shapes run a plain
+ * wave-per-head kernel.
  * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE (num_heads % num_kv_heads != 0, sizes
  * < 1, partition_size not a positive multiple of block_size, max_partitions
  * < 1 in split mode), PKV_ERR_DTYPE, PKV_ERR_UNSUPPORTED (head_size > 256),
@@ -154,13 +160,15 @@ int paged_decode_attention(float* out, const void* query, const void* k_cache,
 /*
  * paged_attention_reduce -- merge split partials into the final output.
  *
- * For each (s, h) with n = ceil(ctx_s / partition_size) partitions (n is
- * clamped to max_partitions), M = max_p m_p and w_p = l_p * exp(m_p - M):
- *   out[s][h][:] = sum_p w_p o_p / sum_p w_p,   out = 0 when n == 0.
- * The pages name only "a reduce kernel that merges the partitions"
- * (source-walkthrough page, section 1.8); this is the exact log-sum-exp merge
- * of the partials paged_decode_attention writes. Partition slots p >= n are
- * never read. Layouts as in paged_decode_attention.
+ * For each (s, h) with ctx_s >= 1, over the slots p < max_partitions with
+ * l_p > 0, M = max_p m_p and w_p = l_p * exp(m_p - M):
+ *   out[s][h][:] = sum_p w_p o_p / sum_p w_p,
+ * and out = 0 when ctx_s <= 0 or no slot is used (nothing is read then).
+ * tmp_out rows of unused slots are never read. The pages name only "a reduce
+ * kernel that merges the partitions" (source-walkthrough page, section 1.8);
+ * this is the exact log-sum-exp merge of the partials paged_decode_attention
+ * writes. partition_size is accepted for symmetry and must be >= 1. Layouts
+ * as in paged_decode_attention.
  * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_LAUNCH. num_seqs == 0 is a
  * no-op.
  */

@@ -9,31 +9,38 @@
 // (running max / running sum) softmax, as FlashAttention-style tiling does
 // (paper-notes page, FlashAttention vs PagedAttention).
 //
-// Work decomposition: one workgroup of NW waves per (sequence, KV head,
-// partition). A partition is `partition_size` positions (split mode, the
-// source-walkthrough page's V2 grid) or the whole context. Positions are
-// processed in tiles of 16 consecutive positions = B/16 tiles per physical
-// block; wave w takes tiles w, w+NW, ... and keeps its own running (m, l,
-// acc); the waves merge through LDS at the end.
-//
-// Per tile (16 positions x 128 dims of one KV head, 4 KiB for 16-bit data):
+// Positions are processed in tiles of 16 consecutive positions (B/16 tiles
+// per physical block). Per tile (16 positions x 128 dims of one KV head,
+// 4 KiB of K and 4 KiB of V for 16-bit data):
 //  * K: lane (row r = lane%16, group j = lane/16) loads 16 B of row r at dim
 //    chunk 4*kk + j for kk = 0..3; each load instruction covers 16 rows x
 //    64 contiguous bytes. Those registers are the A operand of four
 //    v_mfma_f32_16x16x32 (bf16/f16): S = K_tile . Q^T, where Q^T (the B
 //    operand, lane (col n = lane%16, group j) holding q[n] at the same dim
-//    chunk) stays in registers for the whole workgroup. Column n is query head
-//    kv*G + n; columns n >= G hold zeros. The dot-product order over dims is a
-//    fixed permutation shared by both operands, so any k-ordering the matrix
-//    core uses gives the same sum.
+//    chunk) stays in registers. Column n is query head kv*G + n; columns
+//    n >= G hold zeros. The dot-product order over dims is a fixed
+//    permutation shared by both operands, so any k-ordering the matrix core
+//    uses gives the same sum.
 //  * S lands as lane (col n, group j), register i -> position 4j + i. The
-//    tile max per column needs one in-lane max over i and two cross-group
+//    tile max per column needs one in-lane max over i and two cross-row
 //    swaps; exp2 of pre-scaled scores runs on v_exp_f32.
 //  * V: lane (dim chunk c = lane%16, group j) loads 16 B of rows 4j + i
 //    (i = 0..3), each load covering 4 rows x 256 contiguous bytes. The
 //    probability of row 4j+i for head n lives in lane 16j + n of the same
 //    16-lane DPP row, so `row_newbcast:n` broadcasts it and P.V accumulates in
 //    fp32 on the VALU (P is never rounded to 16 bits).
+//
+// Two ways to share the work:
+//  * whole context (no split): one 4-wave workgroup per (sequence, KV head),
+//    waves take every 4th tile and merge through LDS (the single-pass "V1"
+//    grid of the source-walkthrough page, section 1.8, per KV head);
+//  * split (the "V2" partitions of the same section, balanced): a persistent
+//    grid of exactly the resident waves. For each KV head the stream of all
+//    sequences' tiles is cut into equal ranges, one per wave; a wave streams
+//    its range without stopping, ending a piece (one partial) wherever a
+//    sequence or its range ends. Waves with the same range and different KV
+//    heads run side by side, so the KV heads of a physical block (contiguous
+//    in the pool) are read at about the same time.
 #include <type_traits>
 
 #include "device.h"
@@ -42,9 +49,11 @@
 namespace pkv {
 namespace {
 
-constexpr int kD = 128;     // head size of this path
-constexpr int kTile = 16;   // positions per tile
+constexpr int kD = 128;           // head size of this path
+constexpr int kTile = 16;         // positions per tile
 constexpr int kWavesUnsplit = 4;  // waves per (sequence, KV head) without a split
+constexpr int kSplitThreads = 256;
+constexpr int kMaxSeqsBalanced = 8192;  // LDS prefix capacity of the split kernel
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -116,101 +125,81 @@ struct TileRegs {
   uint4 v[4];
 };
 
-__device__ __forceinline__ void load_tile(TileRegs& t, const char* __restrict__ kbase,
-                                          const char* __restrict__ vbase, int k_off,
-                                          int v_off) {
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    t.k[kk] = *reinterpret_cast<const uint4*>(kbase + k_off + kk * 64);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    t.v[i] = *reinterpret_cast<const uint4*>(vbase + v_off + i * 256);
-}
+// Pool geometry and the lane's byte offsets inside a 16-row tile.
+struct Geo {
+  const char* __restrict__ kc;
+  const char* __restrict__ vc;
+  int64_t head_stride;   // bytes per (block, KV head) slab
+  int64_t block_stride;  // bytes per block
+  int B;
+  int max_blocks;
+  int64_t num_blocks;
+  int k_off;  // row `col`, chunk `grp` (+64 B per kk)
+  int v_off;  // rows 4*grp.., chunk `col` (+256 B per i)
 
-// NW waves share one (sequence, KV head, partition) item and merge through
-// LDS (NW = 4, used without a split), or each 64-lane workgroup is one item
-// (NW = 1, used with a split: each wave owns a whole partition, so the
-// serial start of an item -- length, table entry, first tile -- is paid once
-// per partition, and no barrier is needed).
-template <typename T, int GM, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_fast_kernel(DecodeArgs a) {
-  const int lane = threadIdx.x & 63;
-  // wave index, made visibly uniform so table reads become scalar loads
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15;  // K row / score column (head) / V dim chunk
-  const int grp = lane >> 4;  // row group j
+  __device__ Geo(const DecodeArgs& a, int col, int grp)
+      : kc(static_cast<const char*>(a.k_cache)),
+        vc(static_cast<const char*>(a.v_cache)),
+        head_stride(static_cast<int64_t>(a.block_size) * kD * 2),
+        block_stride(static_cast<int64_t>(a.block_size) * kD * 2 * a.num_kv_heads),
+        B(a.block_size),
+        max_blocks(a.max_blocks),
+        num_blocks(a.num_blocks),
+        k_off(col * (kD * 2) + grp * 16),
+        v_off((4 * grp) * (kD * 2) + col * 16) {}
 
-  // Item order: KV head fastest, then sequence, then partition. Workgroups
-  // that run at the same time then read the KV heads of the same physical
-  // blocks, which sit next to each other in the pool (Hkv * B * D contiguous
-  // elements per block), and every sequence's first partitions go first.
-  const int item = blockIdx.x;
-  const int kvh = item % a.num_kv_heads;
-  const int seq = (item / a.num_kv_heads) % a.num_seqs;
-  const int part = item / (a.num_kv_heads * a.num_seqs);
-  const int G = a.num_heads / a.num_kv_heads;
-  const int B = a.block_size;
-
-  int ctx = a.context_lens[seq];
-  const int cap = a.max_blocks * B;
-  ctx = ctx < cap ? ctx : cap;
-  int lo = 0, hi = ctx;
-  if (a.partition_size > 0) {
-    lo = part * a.partition_size;
-    if (lo >= ctx) return;  // this partition does not exist for this sequence
-    hi = lo + a.partition_size < ctx ? lo + a.partition_size : ctx;
-  }
-  const int n_tiles = (hi - lo + kTile - 1) / kTile;
-  const int my_n = n_tiles > w ? (n_tiles - w + NW - 1) / NW : 0;
-
-  const int32_t* __restrict__ row = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
-  const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
-  const char* __restrict__ vc = static_cast<const char*>(a.v_cache);
-  const int64_t head_stride = static_cast<int64_t>(B) * kD * 2;        // bytes per (block, head)
-  const int64_t block_stride = head_stride * a.num_kv_heads;           // bytes per block
-
-  // Q^T operand: lane (col n, group j) holds q[n] dims of chunks 4*kk + j.
-  uint4 qreg[4];
-  {
-    const char* qp = static_cast<const char*>(a.query) +
-                     ((static_cast<int64_t>(seq) * a.num_heads + kvh * G + col) * kD) * 2;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      qreg[kk] = col < G ? *reinterpret_cast<const uint4*>(qp + (4 * kk + grp) * 16)
-                         : make_uint4(0, 0, 0, 0);
-    }
-  }
-  const float qk_scale = a.scale * kLog2e;  // scores kept in log2 units
-
-  // lane offsets inside a 16-row tile (bytes)
-  const int k_off = col * (kD * 2) + grp * 16;     // row col, chunk grp (+64 B per kk)
-  const int v_off = (4 * grp) * (kD * 2) + col * 16;  // rows 4j.., chunk col (+256 B per i)
-
-  float m_run = -INFINITY;  // running max of column `col` (log2 units)
-  float l_part = 0.f;       // running sum over this lane's rows
-  float acc[GM][8];
-#pragma unroll
-  for (int n = 0; n < GM; ++n)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[n][e] = 0.f;
-
-  // Issue the loads of tile ti. Returns false when the table entry is outside
-  // the pool: block 0 is loaded instead (in bounds) and the tile is masked.
-  auto load = [&](TileRegs& t, int ti) -> bool {
-    const int tok0 = lo + (w + NW * ti) * kTile;
-    const int64_t blk = physical_block(row, tok0, B, a.max_blocks, a.num_blocks);
+  // Issue the loads of the tile starting at position tok0 of the sequence
+  // whose table row is `row`. Returns false when the table entry is outside
+  // the pool: block 0 is loaded instead (in bounds) and the caller masks it.
+  __device__ __forceinline__ bool load(TileRegs& t, const int32_t* __restrict__ row, int tok0,
+                                       int kvh) const {
+    const int64_t blk = physical_block(row, tok0, B, max_blocks, num_blocks);
     const int64_t base = (blk < 0 ? 0 : blk) * block_stride + kvh * head_stride +
                          static_cast<int64_t>(tok0 % B) * kD * 2;
-    load_tile(t, kc + base, vc + base, k_off, v_off);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      t.k[kk] = *reinterpret_cast<const uint4*>(kc + base + k_off + kk * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      t.v[i] = *reinterpret_cast<const uint4*>(vc + base + v_off + i * 256);
     return blk >= 0;
-  };
+  }
+};
 
-  auto process = [&](const TileRegs& t, int ti, bool good) {
-    const int tok0 = lo + (w + NW * ti) * kTile;
-    const int lim = good ? hi - tok0 : 0;  // rows >= lim are masked
+// Q^T operand of (sequence seq, KV head kvh): lane (col n, group j) holds
+// q[kvh*G + n] at dim chunks 4*kk + j; zero for n >= G.
+__device__ __forceinline__ void load_q(uint4* q, const DecodeArgs& a, int seq, int kvh, int G,
+                                       int col, int grp) {
+  const char* qp = static_cast<const char*>(a.query) +
+                   ((static_cast<int64_t>(seq) * a.num_heads + kvh * G + col) * kD) * 2;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    q[kk] = col < G ? *reinterpret_cast<const uint4*>(qp + (4 * kk + grp) * 16)
+                    : make_uint4(0, 0, 0, 0);
+}
+
+// Running softmax state of one wave for the G (<= GM) heads of a KV head.
+template <typename T, int GM>
+struct Softmax {
+  float m_run;   // running max of column `col` (log2 units), equal across groups
+  float l_part;  // running sum over this lane's rows of column `col`
+  float acc[GM][8];
+
+  __device__ __forceinline__ void reset() {
+    m_run = -INFINITY;
+    l_part = 0.f;
+#pragma unroll
+    for (int n = 0; n < GM; ++n)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[n][e] = 0.f;
+  }
+
+  // One tile; rows >= lim are masked (their K/V may hold anything, NaN too).
+  __device__ __forceinline__ void tile(const TileRegs& t, const uint4* q, int lim,
+                                       float qk_scale, int grp) {
     f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) S = mfma_k32<T>(t.k[kk], qreg[kk], S);
+    for (int kk = 0; kk < 4; ++kk) S = mfma_k32<T>(t.k[kk], q[kk], S);
     float s[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] = (4 * grp + i < lim) ? S[i] * qk_scale : -INFINITY;
@@ -225,7 +214,6 @@ __global__ __launch_bounds__(NW * 64) void decode_fast_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - m_use);
     l_part = l_part * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
 
-    // rescale, then accumulate P.V for this lane's dims
     static_for<0, GM>([&](auto nc) {
       constexpr int n = decltype(nc)::value;
       const float an = row_bcast<n>(alpha);
@@ -236,7 +224,7 @@ __global__ __launch_bounds__(NW * 64) void decode_fast_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) {
       float vf[8];
       widen8<T>(t.v[i], vf);
-      if (lim < kTile) {  // tail tile: masked rows may hold anything (NaN)
+      if (lim < kTile) {
         const bool ok = 4 * grp + i < lim;
 #pragma unroll
         for (int e = 0; e < 8; ++e) vf[e] = ok ? vf[e] : 0.f;
@@ -248,131 +236,362 @@ __global__ __launch_bounds__(NW * 64) void decode_fast_kernel(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) acc[n][e] = fmaf(pn, vf[e], acc[n][e]);
       });
     }
-  };
+  }
 
-  // software pipeline: the next tile's loads are in flight while this one
-  // is computed (two register sets, unrolled by two to avoid copies)
-  // (every processed tile has either exactly one tile of loads issued after
-  // it or none, on every path, so the wait before it is precise)
+  // Sum the four row groups (same running max per column): afterwards every
+  // lane holds acc[n][dims 8*col..] over all rows, and l_part the column sum.
+  __device__ __forceinline__ void fold_rows() {
+#pragma unroll
+    for (int n = 0; n < GM; ++n)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[n][e] = sum_xor32(sum_xor16(acc[n][e]));
+    l_part = sum_xor32(sum_xor16(l_part));
+  }
+};
+
+// ---------------------------------------------------------------------------
+// whole context: 4 waves per (sequence, KV head)
+// ---------------------------------------------------------------------------
+
+template <typename T, int GM>
+__global__ __launch_bounds__(kWavesUnsplit * 64) void decode_whole_kernel(DecodeArgs a) {
+  constexpr int NW = kWavesUnsplit;
+  const int lane = threadIdx.x & 63;
+  // wave index, made visibly uniform so table reads become scalar loads
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  // KV head fastest: workgroups running together read the KV heads of the
+  // same physical blocks, which are contiguous in the pool
+  const int kvh = blockIdx.x % a.num_kv_heads;
+  const int seq = blockIdx.x / a.num_kv_heads;
+  const int G = a.num_heads / a.num_kv_heads;
+
+  int ctx = a.context_lens[seq];
+  const int cap = a.max_blocks * a.block_size;
+  ctx = ctx < cap ? ctx : cap;
+  const int n_tiles = ctx > 0 ? (ctx + kTile - 1) / kTile : 0;
+  const int my_n = n_tiles > w ? (n_tiles - w + NW - 1) / NW : 0;
+  const int32_t* __restrict__ row = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
+  const Geo geo(a, col, grp);
+  uint4 q[4];
+  load_q(q, a, seq, kvh, G, col, grp);
+  const float qk_scale = a.scale * kLog2e;
+
+  Softmax<T, GM> st;
+  st.reset();
+  auto tok = [&](int ti) { return (w + NW * ti) * kTile; };
+
+  // The next tile's loads are in flight while this one is computed (two
+  // register sets, unrolled by two). Every processed tile has either exactly
+  // one tile of loads issued after it or none on every path, so the wait
+  // before it is exact.
   TileRegs ta, tb;
   bool ga = true, gb = true;
-  if (my_n > 0) ga = load(ta, 0);
+  if (my_n > 0) ga = geo.load(ta, row, tok(0), kvh);
   int ti = 0;
   for (; ti + 1 < my_n; ti += 2) {
-    gb = load(tb, ti + 1);
-    process(ta, ti, ga);
+    gb = geo.load(tb, row, tok(ti + 1), kvh);
+    st.tile(ta, q, ga ? ctx - tok(ti) : 0, qk_scale, grp);
     if (ti + 2 < my_n) {
-      ga = load(ta, ti + 2);
-      process(tb, ti + 1, gb);
+      ga = geo.load(ta, row, tok(ti + 2), kvh);
+      st.tile(tb, q, gb ? ctx - tok(ti + 1) : 0, qk_scale, grp);
     } else {
-      process(tb, ti + 1, gb);
+      st.tile(tb, q, gb ? ctx - tok(ti + 1) : 0, qk_scale, grp);
     }
   }
-  if (ti < my_n) process(ta, ti, ga);
+  if (ti < my_n) st.tile(ta, q, ga ? ctx - tok(ti) : 0, qk_scale, grp);
+  st.fold_rows();
 
-  // merge the four row groups of this wave (same running max per column)
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  __shared__ float sm_acc[NW][GM][kD];
+  if (grp == 0) {
+    sm_m[w][col] = st.m_run;
+    sm_l[w][col] = st.l_part;
 #pragma unroll
-  for (int n = 0; n < GM; ++n)
+    for (int n = 0; n < GM; ++n)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[n][e] = sum_xor32(sum_xor16(acc[n][e]));
-  l_part = sum_xor32(sum_xor16(l_part));
-
+      for (int e = 0; e < 8; ++e) sm_acc[w][n][col * 8 + e] = st.acc[n][e];
+  }
+  __syncthreads();
   const int64_t out_row0 = static_cast<int64_t>(seq) * a.num_heads + kvh * G;
-  if constexpr (NW == 1) {
-    // lane (0, n) holds column n's running max and sum; every lane holds
-    // acc[n][dims 8*col..8*col+7] for all heads n
-    static_for<0, GM>([&](auto nc) {
-      constexpr int n = decltype(nc)::value;
-      if (n < G) {
-        const float ln = row_bcast<n>(l_part);
-        float o[8];
+  for (int idx = threadIdx.x; idx < G * kD; idx += NW * 64) {
+    const int n = idx / kD;
+    const int d = idx % kD;
+    float M = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = ln > 0.f ? acc[n][e] / ln : 0.f;
-        float* dst = a.partition_size > 0
-                         ? a.tmp_out + ((out_row0 + n) * a.max_partitions + part) * kD
-                         : a.out + (out_row0 + n) * kD;
-        if (grp == 0) {
-          reinterpret_cast<float4*>(dst + col * 8)[0] = make_float4(o[0], o[1], o[2], o[3]);
-          reinterpret_cast<float4*>(dst + col * 8)[1] = make_float4(o[4], o[5], o[6], o[7]);
-        }
-      }
-    });
-    if (a.partition_size > 0 && grp == 0 && col < G) {
-      const int64_t pidx = (out_row0 + col) * a.max_partitions + part;
-      a.max_logits[pidx] = m_run * kLn2;  // back to natural-log units
-      a.exp_sums[pidx] = l_part;
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][n]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float den = 0.f, num = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = fast_exp2(sm_m[ww][n] - Mu);
+      den = fmaf(f, sm_l[ww][n], den);
+      num = fmaf(f, sm_acc[ww][n][d], num);
     }
-  } else {
-    // merge the waves through LDS
-    __shared__ float sm_m[NW][16];
-    __shared__ float sm_l[NW][16];
-    __shared__ float sm_acc[NW][GM][kD];
-    if (grp == 0) {
-      sm_m[w][col] = m_run;
-      sm_l[w][col] = l_part;
-#pragma unroll
-      for (int n = 0; n < GM; ++n)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm_acc[w][n][col * 8 + e] = acc[n][e];
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * kD; idx += NW * 64) {
-      const int n = idx / kD;
-      const int d = idx % kD;
-      float M = -INFINITY;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][n]);
-      const float Mu = M == -INFINITY ? 0.f : M;
-      float den = 0.f, num = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float f = fast_exp2(sm_m[ww][n] - Mu);
-        den = fmaf(f, sm_l[ww][n], den);
-        num = fmaf(f, sm_acc[ww][n][d], num);
-      }
-      const float o = den > 0.f ? num / den : 0.f;
-      if (a.partition_size > 0) {
-        const int64_t pidx = (out_row0 + n) * a.max_partitions + part;
-        a.tmp_out[pidx * kD + d] = o;
-        if (d == 0) {
-          a.max_logits[pidx] = M * kLn2;  // back to natural-log units
-          a.exp_sums[pidx] = den;
-        }
-      } else {
-        a.out[(out_row0 + n) * kD + d] = o;
-      }
-    }
+    a.out[(out_row0 + n) * kD + d] = den > 0.f ? num / den : 0.f;
   }
 }
 
-template <typename T, int NW>
-hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
+// ---------------------------------------------------------------------------
+// split: persistent, balanced over tiles
+// ---------------------------------------------------------------------------
+
+// A tile of the per-KV-head stream: sequence s, tile t of its n tiles.
+struct Cursor {
+  int s, t, n, ctx;
+};
+
+template <typename T, int GM>
+__global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs a,
+                                                                     int waves_per_kv) {
+  __shared__ int s_pre[kMaxSeqsBalanced + 1];  // tiles before sequence s
+  __shared__ int s_max[kSplitThreads / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int S = a.num_seqs;
   const int G = a.num_heads / a.num_kv_heads;
-  const int parts = a.partition_size > 0 ? a.max_partitions : 1;
-  const int64_t items = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * parts;
-  dim3 grid(static_cast<unsigned>(items));
-  dim3 block(NW * 64);
-  if (G <= 1) decode_fast_kernel<T, 1, NW><<<grid, block, 0, stream>>>(a);
-  else if (G <= 2) decode_fast_kernel<T, 2, NW><<<grid, block, 0, stream>>>(a);
-  else if (G <= 4) decode_fast_kernel<T, 4, NW><<<grid, block, 0, stream>>>(a);
-  else if (G <= 8) decode_fast_kernel<T, 8, NW><<<grid, block, 0, stream>>>(a);
-  else decode_fast_kernel<T, 16, NW><<<grid, block, 0, stream>>>(a);
+  const int mp = a.max_partitions;
+  const int cap = a.max_blocks * a.block_size;
+
+  // 1. tiles per sequence and their exclusive prefix (every workgroup builds
+  //    the same table; it is tiny next to the KV stream)
+  const int per = (S + kSplitThreads - 1) / kSplitThreads;
+  const int s_lo = tid * per;
+  int local = 0, nmax = 0;
+  for (int i = 0; i < per; ++i) {
+    const int s = s_lo + i;
+    if (s < S) {
+      int c = a.context_lens[s];
+      c = c < cap ? c : cap;
+      const int nt = c > 0 ? (c + kTile - 1) / kTile : 0;
+      local += nt;
+      nmax = nt > nmax ? nt : nmax;
+    }
+  }
+  int incl = local;  // inclusive scan over the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  const int wave_total = __shfl(incl, 63, 64);
+  int wmax = nmax;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int y = __shfl_xor(wmax, off, 64);
+    wmax = y > wmax ? y : wmax;
+  }
+  __shared__ int s_wsum[kSplitThreads / 64];
+  if (lane == 0) {
+    s_wsum[w] = wave_total;
+    s_max[w] = wmax;
+  }
+  __syncthreads();
+  int base = 0, T1 = 0, n_max = 0;
+#pragma unroll
+  for (int i = 0; i < kSplitThreads / 64; ++i) {
+    base += i < w ? s_wsum[i] : 0;
+    T1 += s_wsum[i];
+    n_max = s_max[i] > n_max ? s_max[i] : n_max;
+  }
+  {
+    int run = base + incl - local;  // exclusive prefix of this thread's chunk
+    for (int i = 0; i < per; ++i) {
+      const int s = s_lo + i;
+      if (s < S) {
+        s_pre[s] = run;
+        int c = a.context_lens[s];
+        c = c < cap ? c : cap;
+        run += c > 0 ? (c + kTile - 1) / kTile : 0;
+      }
+    }
+    if (tid == 0) s_pre[S] = T1;
+  }
+  __syncthreads();
+  if (T1 == 0) return;
+
+  // 2. this wave's KV head and range of the stream. Ranges hold at least
+  //    q_min tiles so that no sequence is cut into more than max_partitions
+  //    pieces: a sequence of n tiles meets at most ceil((n-1)/q_min) + 1.
+  const int gw = blockIdx.x * (kSplitThreads / 64) + w;
+  const int kvh = gw % a.num_kv_heads;
+  const int k = gw / a.num_kv_heads;
+  int64_t Wk = waves_per_kv;
+  if (mp >= 2) {
+    const int q_min = n_max > 1 ? (n_max - 1 + mp - 2) / (mp - 1) : 1;
+    const int64_t lim = T1 / q_min;
+    Wk = Wk < lim ? Wk : lim;
+  } else {
+    Wk = 1;
+  }
+  Wk = Wk < 1 ? 1 : Wk;
+  if (k >= Wk) return;
+  const int b0 = static_cast<int>(static_cast<int64_t>(k) * T1 / Wk);
+  const int b1 = static_cast<int>(static_cast<int64_t>(k + 1) * T1 / Wk);
+  const int len = b1 - b0;  // >= 1 since Wk <= T1
+  // range holding stream tile x: largest r with floor(r*T1/Wk) <= x
+  auto range_of = [&](int x) {
+    return static_cast<int>(((static_cast<int64_t>(x) + 1) * Wk - 1) / T1);
+  };
+
+  // sequence holding tile b0: largest s with s_pre[s] <= b0
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= b0) lo = mid; else hi = mid - 1;
+  }
+  auto seq_ctx = [&](int s) {
+    int c = a.context_lens[s];
+    return c < cap ? c : cap;
+  };
+  Cursor cur{lo, b0 - s_pre[lo], s_pre[lo + 1] - s_pre[lo], seq_ctx(lo)};
+  int piece = k - range_of(s_pre[lo]);  // index of this wave's piece of cur.s
+
+  auto advance = [&](const Cursor& c) {
+    if (c.t + 1 < c.n) return Cursor{c.s, c.t + 1, c.n, c.ctx};
+    int s = c.s + 1;
+    while (s < S - 1 && s_pre[s + 1] == s_pre[s]) ++s;  // sequences with no positions
+    return Cursor{s, 0, s_pre[s + 1] - s_pre[s], seq_ctx(s)};
+  };
+  auto row_of = [&](int s) { return a.block_table + static_cast<int64_t>(s) * a.max_blocks; };
+
+  const Geo geo(a, col, grp);
+  const float qk_scale = a.scale * kLog2e;
+  uint4 q[4], qn[4];
+  load_q(q, a, cur.s, kvh, G, col, grp);
+  Softmax<T, GM> st;
+  st.reset();
+
+  // write this piece's partial; after a sequence's last piece, mark the
+  // remaining slots unused (l = 0) so the merge skips them
+  auto finish = [&](const Cursor& c) {
+    st.fold_rows();
+    const int64_t row0 = static_cast<int64_t>(c.s) * a.num_heads + kvh * G;
+    if (piece < mp) {
+      static_for<0, GM>([&](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        if (n < G) {
+          const float ln = row_bcast<n>(st.l_part);
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = ln > 0.f ? st.acc[n][e] / ln : 0.f;
+          float* dst = a.tmp_out + ((row0 + n) * mp + piece) * kD + col * 8;
+          if (grp == 0) {
+            reinterpret_cast<float4*>(dst)[0] = make_float4(o[0], o[1], o[2], o[3]);
+            reinterpret_cast<float4*>(dst)[1] = make_float4(o[4], o[5], o[6], o[7]);
+          }
+        }
+      });
+      if (grp == 0 && col < G) {
+        a.max_logits[(row0 + col) * mp + piece] = st.m_run * kLn2;  // natural-log units
+        a.exp_sums[(row0 + col) * mp + piece] = st.l_part;
+      }
+    }
+    if (c.t == c.n - 1 && grp == 0 && col < G) {
+      for (int p = piece + 1; p < mp; ++p) {
+        a.max_logits[(row0 + col) * mp + p] = -INFINITY;
+        a.exp_sums[(row0 + col) * mp + p] = 0.f;
+      }
+    }
+    st.reset();
+    piece = 0;
+  };
+
+  // Two register sets, unrolled by two; the q of the next sequence is loaded
+  // before that sequence's first tile, ahead of the tile loads, so a wait for
+  // a tile also covers it. Each processed tile has exactly one tile of loads
+  // behind it, or none, on every path.
+  TileRegs ta, tb;
+  bool ga = geo.load(ta, row_of(cur.s), cur.t * kTile, kvh);
+  bool gb = true;
+  Cursor nx = cur;
+  int i = 0;
+  auto step = [&](TileRegs& now, bool g_now, TileRegs& next, bool& g_next) {
+    // now = tile i (cur), next <- tile i + 1
+    const bool more = i + 1 < len;
+    const bool switch_seq = more && (cur.t + 1 >= cur.n);
+    if (more) {
+      nx = advance(cur);
+      if (switch_seq) load_q(qn, a, nx.s, kvh, G, col, grp);
+      g_next = geo.load(next, row_of(nx.s), nx.t * kTile, kvh);
+      st.tile(now, q, g_now ? cur.ctx - cur.t * kTile : 0, qk_scale, grp);
+    } else {
+      st.tile(now, q, g_now ? cur.ctx - cur.t * kTile : 0, qk_scale, grp);
+    }
+    if (cur.t + 1 >= cur.n || !more) finish(cur);
+    if (switch_seq) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) q[kk] = qn[kk];
+    }
+    cur = nx;
+    ++i;
+    return more;
+  };
+  while (true) {
+    if (!step(ta, ga, tb, gb)) break;
+    if (!step(tb, gb, ta, ga)) break;
+  }
+}
+
+template <typename T, int GM>
+hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
+  auto kernel = decode_split_kernel<T, GM>;
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kSplitThreads, 0);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) per_cu = 1;
+  const int waves_per_wg = kSplitThreads / 64;
+  // whole groups of num_kv_heads waves, no more than the GPU holds at once
+  int64_t waves = static_cast<int64_t>(cus) * per_cu * waves_per_wg;
+  int64_t per_kv = waves / a.num_kv_heads;
+  if (per_kv < 1) per_kv = 1;
+  const int64_t wgs = (per_kv * a.num_kv_heads + waves_per_wg - 1) / waves_per_wg;
+  kernel<<<dim3(static_cast<unsigned>(wgs)), dim3(kSplitThreads), 0, stream>>>(
+      a, static_cast<int>(per_kv));
   return hipGetLastError();
+}
+
+template <typename T, int GM>
+hipError_t launch_whole(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t items = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads;
+  decode_whole_kernel<T, GM><<<dim3(static_cast<unsigned>(items)), dim3(kWavesUnsplit * 64), 0,
+                               stream>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, int GM>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  return a.partition_size > 0 ? launch_split<T, GM>(a, stream) : launch_whole<T, GM>(a, stream);
 }
 
 template <typename T>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  return a.partition_size > 0 ? launch_nw<T, 1>(a, stream) : launch_nw<T, kWavesUnsplit>(a, stream);
+  const int G = a.num_heads / a.num_kv_heads;
+  if (G <= 1) return launch_g<T, 1>(a, stream);
+  if (G <= 2) return launch_g<T, 2>(a, stream);
+  if (G <= 4) return launch_g<T, 4>(a, stream);
+  if (G <= 8) return launch_g<T, 8>(a, stream);
+  return launch_g<T, 16>(a, stream);
 }
 
 }  // namespace
 
 bool fast_decode_supported(const DecodeArgs& a) {
   const int G = a.num_heads / a.num_kv_heads;
-  const int64_t parts = a.partition_size > 0 ? a.max_partitions : 1;
-  const int64_t items = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * parts;
-  return (a.dtype == 1 || a.dtype == 2) && a.head_size == kD && a.block_size % kTile == 0 &&
-         G >= 1 && G <= 16 && items <= 0x7fffffff;
+  const int64_t items = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads;
+  if (!((a.dtype == 1 || a.dtype == 2) && a.head_size == kD && a.block_size % kTile == 0 &&
+        G >= 1 && G <= 16 && items <= 0x7fffffff))
+    return false;
+  // the split kernel keeps a per-sequence prefix in LDS
+  return a.partition_size == 0 || a.num_seqs <= kMaxSeqsBalanced;
 }
 
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream) {

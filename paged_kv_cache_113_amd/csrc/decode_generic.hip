@@ -34,7 +34,14 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
   int lo = 0, hi = ctx;
   if (a.partition_size > 0) {
     lo = part * a.partition_size;
-    if (lo >= ctx) return;
+    if (lo >= ctx) {  // no positions here: mark the slot unused for the merge
+      if (lane == 0) {
+        const int64_t pidx = (static_cast<int64_t>(seq) * a.num_heads + h) * a.max_partitions + part;
+        a.max_logits[pidx] = -INFINITY;
+        a.exp_sums[pidx] = 0.f;
+      }
+      return;
+    }
     hi = lo + a.partition_size < ctx ? lo + a.partition_size : ctx;
   }
   const T* __restrict__ q = static_cast<const T*>(a.query) +
@@ -96,17 +103,19 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
 }
 
 // Merge of split partials: one 256-thread workgroup per (sequence, head).
-// The weights w_p = l_p e^{m_p - M} are computed once per partition (all
-// threads in parallel) and staged in LDS in chunks; each wave then
-// accumulates every 4th partition over all dims (lane owns dims lane + 64k,
-// coalesced 4-byte rows), and the four waves' sums meet in LDS.
+// Every slot with l_p > 0 takes part (a real partial has l_p >= 1: its
+// largest score contributes e^0); unused slots carry l_p = 0. The weights
+// w_p = l_p e^{m_p - M} are computed once per slot (all threads in parallel)
+// and staged in LDS in chunks; each wave then accumulates every 4th used slot
+// over all dims (lane owns dims lane + 64k, coalesced 4-byte rows), and the
+// four waves' sums meet in LDS.
 constexpr int kRedThreads = 256;
 constexpr int kRedChunk = 2048;
 
 __global__ __launch_bounds__(kRedThreads) void reduce_kernel(
     float* __restrict__ out, const float* __restrict__ max_logits,
     const float* __restrict__ exp_sums, const float* __restrict__ tmp_out,
-    const int32_t* __restrict__ context_lens, int num_heads, int head_size, int partition_size,
+    const int32_t* __restrict__ context_lens, int num_heads, int head_size,
     int max_partitions) {
   __shared__ float s_w[kRedChunk];
   __shared__ float s_red[kRedThreads / 64];
@@ -118,15 +127,14 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(
   const int seq = blockIdx.y;
   const int D = head_size;
   const int64_t orow = static_cast<int64_t>(seq) * num_heads + h;
-  const int ctx = context_lens[seq];
-  int n = ctx > 0 ? (ctx + partition_size - 1) / partition_size : 0;
-  n = n < max_partitions ? n : max_partitions;
+  const int n = context_lens[seq] > 0 ? max_partitions : 0;
   const float* __restrict__ m = max_logits + orow * max_partitions;
   const float* __restrict__ l = exp_sums + orow * max_partitions;
   const float* __restrict__ o = tmp_out + orow * max_partitions * D;
 
   float mx = -INFINITY;
-  for (int p = tid; p < n; p += kRedThreads) mx = fmaxf(mx, m[p]);
+  for (int p = tid; p < n; p += kRedThreads)
+    if (l[p] > 0.f) mx = fmaxf(mx, m[p]);
   mx = wave_max(mx);
   if (lane == 0) s_red[w] = mx;
   __syncthreads();
@@ -140,7 +148,8 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(
     const int cn = n - c0 < kRedChunk ? n - c0 : kRedChunk;
     __syncthreads();  // previous chunk's weights are no longer read
     for (int p = tid; p < cn; p += kRedThreads) {
-      const float wp = l[c0 + p] * expf(m[c0 + p] - M);
+      const float lp = l[c0 + p];
+      const float wp = lp > 0.f ? lp * expf(m[c0 + p] - M) : 0.f;
       s_w[p] = wp;
       den += wp;
     }
@@ -148,6 +157,7 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(
 #pragma unroll 4
     for (int p = w; p < cn; p += kRedThreads / 64) {
       const float wp = s_w[p];
+      if (wp == 0.f) continue;  // unused slot: its row is never read
       const float* __restrict__ row = o + static_cast<int64_t>(c0 + p) * D;
 #pragma unroll
       for (int k = 0; k < kMaxPerLane; ++k) {
@@ -191,8 +201,9 @@ hipError_t launch_reduce(float* out, const float* max_logits, const float* exp_s
                          int num_heads, int head_size, int partition_size, int max_partitions,
                          hipStream_t stream) {
   dim3 grid(num_heads, num_seqs);
+  (void)partition_size;
   reduce_kernel<<<grid, kRedThreads, 0, stream>>>(out, max_logits, exp_sums, tmp_out, context_lens,
-                                         num_heads, head_size, partition_size, max_partitions);
+                                                  num_heads, head_size, max_partitions);
   return hipGetLastError();
 }
 

@@ -289,3 +289,40 @@ def test_decode_step_full_size_layer(dev, pkv, layer):
     e = max_err(out.cpu()[seqs], want)
     say(f"  sampled {len(seqs)} seqs: max abs err {e:.3e}")
     assert e <= TOL
+
+
+@pytest.mark.parametrize("name,P,mp_override", [
+    ("gqa_shared_bf16", 64, None), ("gqa_shared_bf16", 512, None),
+    ("mha_fp16", 256, 2), ("gqa8_f16", 32, 1), ("long_split_bf16", 512, None)])
+def test_split_slots_contract(dev, pkv, name, P, mp_override):
+    """Split mode writes every slot of every (sequence, head) with ctx >= 1:
+    a partial with l >= 1 or an unused slot with l = 0 and m = -inf; at most
+    max_partitions pieces; and the merge of the used slots is the attention."""
+    b = SMALL[name]()
+    say(f"case: split slots {name} P={P} mp={mp_override}")
+    t = W.layer_tensors(b, device=dev)
+    meta = device_meta(b, dev)
+    mp = b.max_partitions(P) if mp_override is None else mp_override
+    shape = (b.num_seqs, b.num_heads, mp)
+    ml = torch.full(shape, float("nan"), device=dev)
+    es = torch.full(shape, float("nan"), device=dev)
+    to = torch.full(shape + (b.head_size,), float("nan"), device=dev)
+    pkv.paged_decode_attention(None, t["q"], t["k_cache"], t["v_cache"], meta["table"],
+                               meta["ctx"], scale_of(b), P, mp, ml, es, to)
+    out = torch.empty(b.num_seqs, b.num_heads, b.head_size, device=dev)
+    pkv.paged_attention_reduce(out, ml, es, to, meta["ctx"], P)
+    torch.cuda.synchronize()
+    ml, es = ml.cpu(), es.cpu()
+    live = torch.as_tensor(b.context_lens > 0)
+    assert not torch.isnan(es[live]).any() and not torch.isnan(ml[live]).any()
+    used = es > 0
+    assert (es[used] >= 1.0 - 1e-6).all()
+    unused = live[:, None, None] & ~used
+    assert (es[unused] == 0).all() and torch.isinf(ml[unused]).all()
+    # every live (sequence, head) has at least one piece, at most mp
+    assert (used.sum(-1)[live] >= 1).all() and (used.sum(-1) <= mp).all()
+    th = host(t)
+    want = oracle_attention(b, th["q"], th["k_cache"], th["v_cache"])
+    e = max_err(out.cpu(), want)
+    say(f"  max abs err {e:.3e}, pieces per (seq, head) up to {int(used.sum(-1).max())}")
+    assert e <= TOL
