@@ -68,7 +68,7 @@ def make_batch(workload):
 def default_partition(workload):
     """Split size per workload: it sizes the partial slots (max_partitions =
     ceil(max ctx / P)); smaller P leaves the balanced split more freedom."""
-    return {"decode_step_bf16": 256, "long_split_bf16": 512, "mha_fp16": 256,
+    return {"decode_step_bf16": 256, "long_split_bf16": 1024, "mha_fp16": 256,
             "gqa_shared_bf16": 1024, "tiny": 0}[workload]
 
 

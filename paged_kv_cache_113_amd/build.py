@@ -23,6 +23,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops (v_pk_*_f32) stay off: plain fp32 math only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in VGPRs: the attention accumulators are rescaled
+    # on the VALU every tile, so AGPR-resident results would be copied back
+    # and forth
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -11,7 +11,8 @@
 //
 // Positions are processed in tiles of 16 consecutive positions (B/16 tiles
 // per physical block). Per tile (16 positions x 128 dims of one KV head,
-// 4 KiB of K and 4 KiB of V for 16-bit data):
+// 4 KiB of K and 4 KiB of V for 16-bit data), both products run on the
+// matrix cores:
 //  * K: lane (row r = lane%16, group j = lane/16) loads 16 B of row r at dim
 //    chunk 4*kk + j for kk = 0..3; each load instruction covers 16 rows x
 //    64 contiguous bytes. Those registers are the A operand of four
@@ -23,12 +24,17 @@
 //    uses gives the same sum.
 //  * S lands as lane (col n, group j), register i -> position 4j + i. The
 //    tile max per column needs one in-lane max over i and two cross-row
-//    swaps; exp2 of pre-scaled scores runs on v_exp_f32.
+//    swaps (v_permlane{16,32}_swap); exp2 of pre-scaled scores runs on
+//    v_exp_f32. The probabilities of lane (n, j) are exactly the B operand
+//    (P^T, positions 4j..4j+3 of column n) of v_mfma_f32_16x16x16, split
+//    into a 16-bit high part and a 16-bit remainder so that P keeps ~16
+//    significant bits.
 //  * V: lane (dim chunk c = lane%16, group j) loads 16 B of rows 4j + i
-//    (i = 0..3), each load covering 4 rows x 256 contiguous bytes. The
-//    probability of row 4j+i for head n lives in lane 16j + n of the same
-//    16-lane DPP row, so `row_newbcast:n` broadcasts it and P.V accumulates in
-//    fp32 on the VALU (P is never rounded to 16 bits).
+//    (i = 0..3), 4 rows x 256 contiguous bytes per load, and stores them in
+//    the wave's 4 KiB LDS slot (32-byte chunks XOR-swizzled by row against
+//    bank conflicts). ds_read_b64_tr_b16 then hands lane (d, j) the four
+//    positions 4j..4j+3 of dim 16*db + d: the A operand (V^T) of the P.V
+//    product, eight blocks db per tile, accumulated in fp32 as O^T[d][n].
 //
 // Two ways to share the work:
 //  * whole context (no split): one 4-wave workgroup per (sequence, KV head),
@@ -54,25 +60,16 @@ constexpr int kTile = 16;         // positions per tile
 constexpr int kWavesUnsplit = 4;  // waves per (sequence, KV head) without a split
 constexpr int kSplitThreads = 256;
 constexpr int kMaxSeqsBalanced = 8192;  // LDS prefix capacity of the split kernel
+constexpr int kSlotBytes = kTile * kD * 2;  // one wave's V tile in LDS (4 KiB)
+
+#define PKV_LDS __attribute__((address_space(3)))
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-// Broadcast lane N of each 16-lane row to the whole row (DPP row_newbcast).
-template <int N>
-__device__ __forceinline__ float row_bcast(float x) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, false));
-}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // max / sum of x over the lane pairs (l, l ^ 16) and (l, l ^ 32), returned in
 // every lane. v_permlane{16,32}_swap exchange rows between two registers on
@@ -106,18 +103,37 @@ __device__ __forceinline__ f32x4 mfma_k32(uint4 a, uint4 b, f32x4 c) {
 }
 
 template <typename T>
-__device__ __forceinline__ void widen8(uint4 w, float* f) {
-  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+__device__ __forceinline__ f32x4 mfma_k16(uint2 a, uint2 b, f32x4 c) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+}
+
+// p (four probabilities in [0, 1]) as a 16-bit high part and the 16-bit
+// rounding of the remainder: hi + lo = p to about 2^-16 relative.
+template <typename T>
+__device__ __forceinline__ void split_p(const float* p, uint2& hi, uint2& lo) {
+  uint16_t h[4], r[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int i = 0; i < 4; ++i) {
     if constexpr (std::is_same<T, bf16_t>::value) {
-      f[2 * k] = lo_bf16(u[k]);
-      f[2 * k + 1] = hi_bf16(u[k]);
+      const __bf16 a = static_cast<__bf16>(p[i]);
+      const __bf16 b = static_cast<__bf16>(p[i] - static_cast<float>(a));
+      h[i] = __builtin_bit_cast(uint16_t, a);
+      r[i] = __builtin_bit_cast(uint16_t, b);
     } else {
-      f[2 * k] = lo_f16(u[k]);
-      f[2 * k + 1] = hi_f16(u[k]);
+      const _Float16 a = static_cast<_Float16>(p[i]);
+      const _Float16 b = static_cast<_Float16>(p[i] - static_cast<float>(a));
+      h[i] = __builtin_bit_cast(uint16_t, a);
+      r[i] = __builtin_bit_cast(uint16_t, b);
     }
   }
+  hi = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+  lo = make_uint2(r[0] | (uint32_t(r[1]) << 16), r[2] | (uint32_t(r[3]) << 16));
 }
 
 struct TileRegs {
@@ -178,25 +194,32 @@ __device__ __forceinline__ void load_q(uint4* q, const DecodeArgs& a, int seq, i
                     : make_uint4(0, 0, 0, 0);
 }
 
-// Running softmax state of one wave for the G (<= GM) heads of a KV head.
-template <typename T, int GM>
-struct Softmax {
-  float m_run;   // running max of column `col` (log2 units), equal across groups
-  float l_part;  // running sum over this lane's rows of column `col`
-  float acc[GM][8];
+// Byte offset, in a V slot, of 16-byte chunk `chunk` (0..15) of row `row`:
+// rows are 256 B; the 32-byte chunk index is XORed with row % 8.
+__device__ __forceinline__ int slot_offset(int row, int chunk) {
+  return row * (kD * 2) + (((chunk >> 1) ^ (row & 7)) << 5) + ((chunk & 1) << 4);
+}
+
+// Running softmax state of one wave: lane (col n, group j) keeps column n's
+// running max and its partial sum over rows 4j..4j+3, and acc[db][r] =
+// O^T[16*db + 4j + r][n] (unnormalised), for the G (<= 16) heads of a KV head.
+template <typename T>
+struct Attend {
+  float m_run;
+  float l_part;
+  f32x4 acc[8];
 
   __device__ __forceinline__ void reset() {
     m_run = -INFINITY;
     l_part = 0.f;
 #pragma unroll
-    for (int n = 0; n < GM; ++n)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[n][e] = 0.f;
+    for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // One tile; rows >= lim are masked (their K/V may hold anything, NaN too).
+  // `slot` is this wave's 4 KiB of LDS.
   __device__ __forceinline__ void tile(const TileRegs& t, const uint4* q, int lim,
-                                       float qk_scale, int grp) {
+                                       float qk_scale, int grp, int col, PKV_LDS char* slot) {
     f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) S = mfma_k32<T>(t.k[kk], q[kk], S);
@@ -214,38 +237,37 @@ struct Softmax {
     for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - m_use);
     l_part = l_part * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
 
-    static_for<0, GM>([&](auto nc) {
-      constexpr int n = decltype(nc)::value;
-      const float an = row_bcast<n>(alpha);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[n][e] *= an;
-    });
+    // V rows into LDS; on the tail tile masked rows become zeros (P is 0
+    // there, and 0 * NaN would still be NaN)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float vf[8];
-      widen8<T>(t.v[i], vf);
-      if (lim < kTile) {
-        const bool ok = 4 * grp + i < lim;
+      uint4 v = t.v[i];
+      if (lim < kTile && 4 * grp + i >= lim) v = make_uint4(0, 0, 0, 0);
+      *(PKV_LDS u32x4*)(slot + slot_offset(4 * grp + i, col)) = __builtin_bit_cast(u32x4, v);
+    }
+    uint2 phi, plo;
+    split_p<T>(p, phi, plo);
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vf[e] = ok ? vf[e] : 0.f;
-      }
-      static_for<0, GM>([&](auto nc) {
-        constexpr int n = decltype(nc)::value;
-        const float pn = row_bcast<n>(p[i]);
+      for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+    }
+    // lane (d = col, group j): positions 4j..4j+3 of dim 16*db + d, gathered by
+    // the transpose read from rows 4j + col/4, bytes 8*(col%4) of chunk db
+    const int rrow = 4 * grp + (col >> 2);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[n][e] = fmaf(pn, vf[e], acc[n][e]);
-      });
+    for (int db = 0; db < 8; ++db) {
+      const int off = rrow * (kD * 2) + ((db ^ (rrow & 7)) << 5) + ((col & 3) << 3);
+      const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (PKV_LDS s16x4*)(slot + off));
+      const uint2 a = __builtin_bit_cast(uint2, vt);
+      acc[db] = mfma_k16<T>(a, phi, acc[db]);
+      acc[db] = mfma_k16<T>(a, plo, acc[db]);
     }
   }
 
-  // Sum the four row groups (same running max per column): afterwards every
-  // lane holds acc[n][dims 8*col..] over all rows, and l_part the column sum.
-  __device__ __forceinline__ void fold_rows() {
-#pragma unroll
-    for (int n = 0; n < GM; ++n)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[n][e] = sum_xor32(sum_xor16(acc[n][e]));
-    l_part = sum_xor32(sum_xor16(l_part));
+  // Column sum of l over the four row groups, in every lane.
+  __device__ __forceinline__ float column_sum() const {
+    return sum_xor32(sum_xor16(l_part));
   }
 };
 
@@ -253,9 +275,13 @@ struct Softmax {
 // whole context: 4 waves per (sequence, KV head)
 // ---------------------------------------------------------------------------
 
-template <typename T, int GM>
+template <typename T>
 __global__ __launch_bounds__(kWavesUnsplit * 64) void decode_whole_kernel(DecodeArgs a) {
   constexpr int NW = kWavesUnsplit;
+  // V slots during the tile loop; the waves' partial outputs afterwards
+  __shared__ __attribute__((aligned(16))) char smem[NW * 16 * kD * 4];
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
   const int lane = threadIdx.x & 63;
   // wave index, made visibly uniform so table reads become scalar loads
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -277,8 +303,9 @@ __global__ __launch_bounds__(kWavesUnsplit * 64) void decode_whole_kernel(Decode
   uint4 q[4];
   load_q(q, a, seq, kvh, G, col, grp);
   const float qk_scale = a.scale * kLog2e;
+  PKV_LDS char* slot = (PKV_LDS char*)(smem) + w * kSlotBytes;
 
-  Softmax<T, GM> st;
+  Attend<T> st;
   st.reset();
   auto tok = [&](int ti) { return (w + NW * ti) * kTile; };
 
@@ -292,28 +319,27 @@ __global__ __launch_bounds__(kWavesUnsplit * 64) void decode_whole_kernel(Decode
   int ti = 0;
   for (; ti + 1 < my_n; ti += 2) {
     gb = geo.load(tb, row, tok(ti + 1), kvh);
-    st.tile(ta, q, ga ? ctx - tok(ti) : 0, qk_scale, grp);
+    st.tile(ta, q, ga ? ctx - tok(ti) : 0, qk_scale, grp, col, slot);
     if (ti + 2 < my_n) {
       ga = geo.load(ta, row, tok(ti + 2), kvh);
-      st.tile(tb, q, gb ? ctx - tok(ti + 1) : 0, qk_scale, grp);
+      st.tile(tb, q, gb ? ctx - tok(ti + 1) : 0, qk_scale, grp, col, slot);
     } else {
-      st.tile(tb, q, gb ? ctx - tok(ti + 1) : 0, qk_scale, grp);
+      st.tile(tb, q, gb ? ctx - tok(ti + 1) : 0, qk_scale, grp, col, slot);
     }
   }
-  if (ti < my_n) st.tile(ta, q, ga ? ctx - tok(ti) : 0, qk_scale, grp);
-  st.fold_rows();
+  if (ti < my_n) st.tile(ta, q, ga ? ctx - tok(ti) : 0, qk_scale, grp, col, slot);
+  const float l_col = st.column_sum();
 
-  __shared__ float sm_m[NW][16];
-  __shared__ float sm_l[NW][16];
-  __shared__ float sm_acc[NW][GM][kD];
+  __syncthreads();  // every wave is done with its V slot
+  float* sm_acc = reinterpret_cast<float*>(smem);  // [NW][16][kD]
   if (grp == 0) {
     sm_m[w][col] = st.m_run;
-    sm_l[w][col] = st.l_part;
-#pragma unroll
-    for (int n = 0; n < GM; ++n)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[w][n][col * 8 + e] = st.acc[n][e];
+    sm_l[w][col] = l_col;
   }
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    *reinterpret_cast<float4*>(sm_acc + (w * 16 + col) * kD + 16 * db + 4 * grp) =
+        make_float4(st.acc[db][0], st.acc[db][1], st.acc[db][2], st.acc[db][3]);
   __syncthreads();
   const int64_t out_row0 = static_cast<int64_t>(seq) * a.num_heads + kvh * G;
   for (int idx = threadIdx.x; idx < G * kD; idx += NW * 64) {
@@ -328,7 +354,7 @@ __global__ __launch_bounds__(kWavesUnsplit * 64) void decode_whole_kernel(Decode
     for (int ww = 0; ww < NW; ++ww) {
       const float f = fast_exp2(sm_m[ww][n] - Mu);
       den = fmaf(f, sm_l[ww][n], den);
-      num = fmaf(f, sm_acc[ww][n][d], num);
+      num = fmaf(f, sm_acc[(ww * 16 + n) * kD + d], num);
     }
     a.out[(out_row0 + n) * kD + d] = den > 0.f ? num / den : 0.f;
   }
@@ -343,11 +369,13 @@ struct Cursor {
   int s, t, n, ctx;
 };
 
-template <typename T, int GM>
+template <typename T>
 __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs a,
                                                                      int waves_per_kv) {
-  __shared__ int s_pre[kMaxSeqsBalanced + 1];  // tiles before sequence s
+  extern __shared__ int s_pre[];  // [S + 1]: tiles before sequence s
+  __shared__ __attribute__((aligned(16))) char s_slots[(kSplitThreads / 64) * kSlotBytes];
   __shared__ int s_max[kSplitThreads / 64];
+  __shared__ int s_wsum[kSplitThreads / 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -386,7 +414,6 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     const int y = __shfl_xor(wmax, off, 64);
     wmax = y > wmax ? y : wmax;
   }
-  __shared__ int s_wsum[kSplitThreads / 64];
   if (lane == 0) {
     s_wsum[w] = wave_total;
     s_max[w] = wmax;
@@ -462,40 +489,36 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
 
   const Geo geo(a, col, grp);
   const float qk_scale = a.scale * kLog2e;
+  PKV_LDS char* slot = (PKV_LDS char*)(s_slots) + w * kSlotBytes;
   uint4 q[4], qn[4];
   load_q(q, a, cur.s, kvh, G, col, grp);
-  Softmax<T, GM> st;
+  Attend<T> st;
   st.reset();
 
   // write this piece's partial; after a sequence's last piece, mark the
   // remaining slots unused (l = 0) so the merge skips them
   auto finish = [&](const Cursor& c) {
-    st.fold_rows();
+    const float l_col = st.column_sum();
     const int64_t row0 = static_cast<int64_t>(c.s) * a.num_heads + kvh * G;
-    if (piece < mp) {
-      static_for<0, GM>([&](auto nc) {
-        constexpr int n = decltype(nc)::value;
-        if (n < G) {
-          const float ln = row_bcast<n>(st.l_part);
-          float o[8];
+    if (col < G) {
+      if (piece < mp) {
+        const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
+        float* dst = a.tmp_out + ((row0 + col) * mp + piece) * kD + 4 * grp;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = ln > 0.f ? st.acc[n][e] / ln : 0.f;
-          float* dst = a.tmp_out + ((row0 + n) * mp + piece) * kD + col * 8;
-          if (grp == 0) {
-            reinterpret_cast<float4*>(dst)[0] = make_float4(o[0], o[1], o[2], o[3]);
-            reinterpret_cast<float4*>(dst)[1] = make_float4(o[4], o[5], o[6], o[7]);
-          }
+        for (int db = 0; db < 8; ++db)
+          *reinterpret_cast<float4*>(dst + 16 * db) =
+              make_float4(st.acc[db][0] * inv, st.acc[db][1] * inv, st.acc[db][2] * inv,
+                          st.acc[db][3] * inv);
+        if (grp == 0) {
+          a.max_logits[(row0 + col) * mp + piece] = st.m_run * kLn2;  // natural-log units
+          a.exp_sums[(row0 + col) * mp + piece] = l_col;
         }
-      });
-      if (grp == 0 && col < G) {
-        a.max_logits[(row0 + col) * mp + piece] = st.m_run * kLn2;  // natural-log units
-        a.exp_sums[(row0 + col) * mp + piece] = st.l_part;
       }
-    }
-    if (c.t == c.n - 1 && grp == 0 && col < G) {
-      for (int p = piece + 1; p < mp; ++p) {
-        a.max_logits[(row0 + col) * mp + p] = -INFINITY;
-        a.exp_sums[(row0 + col) * mp + p] = 0.f;
+      if (c.t == c.n - 1 && grp == 0) {
+        for (int p = piece + 1; p < mp; ++p) {
+          a.max_logits[(row0 + col) * mp + p] = -INFINITY;
+          a.exp_sums[(row0 + col) * mp + p] = 0.f;
+        }
       }
     }
     st.reset();
@@ -519,9 +542,9 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
       nx = advance(cur);
       if (switch_seq) load_q(qn, a, nx.s, kvh, G, col, grp);
       g_next = geo.load(next, row_of(nx.s), nx.t * kTile, kvh);
-      st.tile(now, q, g_now ? cur.ctx - cur.t * kTile : 0, qk_scale, grp);
+      st.tile(now, q, g_now ? cur.ctx - cur.t * kTile : 0, qk_scale, grp, col, slot);
     } else {
-      st.tile(now, q, g_now ? cur.ctx - cur.t * kTile : 0, qk_scale, grp);
+      st.tile(now, q, g_now ? cur.ctx - cur.t * kTile : 0, qk_scale, grp, col, slot);
     }
     if (cur.t + 1 >= cur.n || !more) finish(cur);
     if (switch_seq) {
@@ -538,14 +561,15 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   }
 }
 
-template <typename T, int GM>
+template <typename T>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
-  auto kernel = decode_split_kernel<T, GM>;
+  auto kernel = decode_split_kernel<T>;
+  const size_t dyn = static_cast<size_t>(a.num_seqs + 1) * sizeof(int);
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kSplitThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kSplitThreads, dyn);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   const int waves_per_wg = kSplitThreads / 64;
@@ -554,32 +578,22 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
   int64_t per_kv = waves / a.num_kv_heads;
   if (per_kv < 1) per_kv = 1;
   const int64_t wgs = (per_kv * a.num_kv_heads + waves_per_wg - 1) / waves_per_wg;
-  kernel<<<dim3(static_cast<unsigned>(wgs)), dim3(kSplitThreads), 0, stream>>>(
+  kernel<<<dim3(static_cast<unsigned>(wgs)), dim3(kSplitThreads), dyn, stream>>>(
       a, static_cast<int>(per_kv));
   return hipGetLastError();
 }
 
-template <typename T, int GM>
+template <typename T>
 hipError_t launch_whole(const DecodeArgs& a, hipStream_t stream) {
   const int64_t items = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads;
-  decode_whole_kernel<T, GM><<<dim3(static_cast<unsigned>(items)), dim3(kWavesUnsplit * 64), 0,
-                               stream>>>(a);
+  decode_whole_kernel<T><<<dim3(static_cast<unsigned>(items)), dim3(kWavesUnsplit * 64), 0,
+                           stream>>>(a);
   return hipGetLastError();
-}
-
-template <typename T, int GM>
-hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
-  return a.partition_size > 0 ? launch_split<T, GM>(a, stream) : launch_whole<T, GM>(a, stream);
 }
 
 template <typename T>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  const int G = a.num_heads / a.num_kv_heads;
-  if (G <= 1) return launch_g<T, 1>(a, stream);
-  if (G <= 2) return launch_g<T, 2>(a, stream);
-  if (G <= 4) return launch_g<T, 4>(a, stream);
-  if (G <= 8) return launch_g<T, 8>(a, stream);
-  return launch_g<T, 16>(a, stream);
+  return a.partition_size > 0 ? launch_split<T>(a, stream) : launch_whole<T>(a, stream);
 }
 
 }  // namespace
