@@ -189,38 +189,38 @@ def main():
 
     ev = {k: [] for k in ("decode", "reduce", "write")}
 
-    def step(record):
+    def timed(name, record, fn):
+        # HIP events on torch's current stream, which is the stream every
+        # library call is enqueued on
+        if name not in record:
+            fn()
+            return
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        ev[name].append((e0, e1))
+
+    def step(record=()):
         if pos is not None:
             pkv.paged_slot_mapping(slots, table, pos, batch.block_size)
         for l, t in enumerate(layers):
             if pos is not None:
-                if record:
-                    e0 = torch.cuda.Event(enable_timing=True); e0.record()
-                pkv.paged_kv_write(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], slots)
-                if record:
-                    e1 = torch.cuda.Event(enable_timing=True); e1.record()
-                    ev["write"].append((e0, e1))
-            if record:
-                e0 = torch.cuda.Event(enable_timing=True); e0.record()
+                timed("write", record, lambda: pkv.paged_kv_write(
+                    t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], slots))
             if P > 0:
-                pkv.paged_decode_attention(None, t["q"], t["k_cache"], t["v_cache"], table, ctx,
-                                           scale, P, mp, ml, es, to)
+                timed("decode", record, lambda: pkv.paged_decode_attention(
+                    None, t["q"], t["k_cache"], t["v_cache"], table, ctx, scale, P, mp, ml, es,
+                    to))
+                timed("reduce", record, lambda: pkv.paged_attention_reduce(
+                    outs[l], ml, es, to, ctx, P))
             else:
-                pkv.paged_decode_attention(outs[l], t["q"], t["k_cache"], t["v_cache"], table,
-                                           ctx, scale)
-            if record:
-                e1 = torch.cuda.Event(enable_timing=True); e1.record()
-                ev["decode"].append((e0, e1))
-            if P > 0:
-                if record:
-                    e0 = torch.cuda.Event(enable_timing=True); e0.record()
-                pkv.paged_attention_reduce(outs[l], ml, es, to, ctx, P)
-                if record:
-                    e1 = torch.cuda.Event(enable_timing=True); e1.record()
-                    ev["reduce"].append((e0, e1))
+                timed("decode", record, lambda: pkv.paged_decode_attention(
+                    outs[l], t["q"], t["k_cache"], t["v_cache"], table, ctx, scale))
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
 
     if args.copy_probe:
@@ -236,7 +236,7 @@ def main():
     t_start = time.perf_counter()
     if flush is None:
         for _ in range(args.steps):
-            step(True)
+            step(("decode",))
         torch.cuda.synchronize()
         total_s = time.perf_counter() - t_start
     else:
@@ -246,10 +246,13 @@ def main():
             flush.sum()
             torch.cuda.synchronize()
             t1 = time.perf_counter()
-            step(True)
+            step(("decode",))
             torch.cuda.synchronize()
             total_s += time.perf_counter() - t1
     ms_per_step = total_s / args.steps * 1e3
+    # the smaller kernels' own durations, from one more (untimed) step
+    step(("write", "reduce"))
+    torch.cuda.synchronize()
 
     def avg_ms(name):
         xs = [a.elapsed_time(b) for a, b in ev[name]]
@@ -259,7 +262,14 @@ def main():
     dec_ms, dec_p10, dec_p90 = avg_ms("decode")
     red_ms = avg_ms("reduce")[0]
     wr_ms = avg_ms("write")[0]
-    layer_bytes = kv_bytes(batch, batch.context_lens)
+    logical_bytes = kv_bytes(batch, batch.context_lens)
+    layer_bytes = logical_bytes
+    if len(batch.sharers) > 1:
+        # a shared prefix block is read once per KV head however many
+        # sequences map it: algorithmic bytes count it once
+        per_pos = logical_bytes / float(np.sum(batch.context_lens, dtype=np.int64))
+        layer_bytes -= (len(batch.sharers) - 1) * len(batch.shared_blocks) * \
+            batch.block_size * per_pos
     step_bytes = layer_bytes * L
     value = step_bytes / (ms_per_step / 1e3) / 1e9
     achieved = layer_bytes / (dec_ms / 1e3) / 1e9
@@ -293,8 +303,9 @@ def main():
                        "write_avg": round(wr_ms, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_fast_kernel",
-                     "bytes_per_launch": layer_bytes},
+                     "traffic": traffic, "kernel": "decode_split_kernel" if P > 0
+                     else "decode_whole_kernel", "bytes_per_launch": layer_bytes,
+                     "logical_bytes_per_launch": logical_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -112,7 +112,8 @@ int paged_attention_reduce(float* out, const float* max_logits, const float* exp
     return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !max_logits || !exp_sums || !tmp_out || !context_lens) return PKV_ERR_NULL;
-  if (num_seqs > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  // one wave per (sequence, head), four per workgroup
+  if (static_cast<int64_t>(num_seqs) * num_heads / 4 >= 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   return launch_status(pkv::launch_reduce(out, max_logits, exp_sums, tmp_out, context_lens,
                                           num_seqs, num_heads, head_size, partition_size,
                                           max_partitions, as_stream(stream)));

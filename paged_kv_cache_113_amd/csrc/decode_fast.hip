@@ -141,6 +141,10 @@ struct TileRegs {
   uint4 v[4];
 };
 
+// Keeps the compiler from moving the next tile's loads below the wait for the
+// current tile: the loads must be in flight while this tile is computed.
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Pool geometry and the lane's byte offsets inside a 16-row tile.
 struct Geo {
   const char* __restrict__ kc;
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(kWavesUnsplit * 64) void decode_whole_kernel(Decode
   const int seq = blockIdx.x / a.num_kv_heads;
   const int G = a.num_heads / a.num_kv_heads;
 
-  int ctx = a.context_lens[seq];
+  int ctx = read_only(a.context_lens + seq);
   const int cap = a.max_blocks * a.block_size;
   ctx = ctx < cap ? ctx : cap;
   const int n_tiles = ctx > 0 ? (ctx + kTile - 1) / kTile : 0;
@@ -319,9 +323,11 @@ __global__ __launch_bounds__(kWavesUnsplit * 64) void decode_whole_kernel(Decode
   int ti = 0;
   for (; ti + 1 < my_n; ti += 2) {
     gb = geo.load(tb, row, tok(ti + 1), kvh);
+    issue_fence();
     st.tile(ta, q, ga ? ctx - tok(ti) : 0, qk_scale, grp, col, slot);
     if (ti + 2 < my_n) {
       ga = geo.load(ta, row, tok(ti + 2), kvh);
+      issue_fence();
       st.tile(tb, q, gb ? ctx - tok(ti + 1) : 0, qk_scale, grp, col, slot);
     } else {
       st.tile(tb, q, gb ? ctx - tok(ti + 1) : 0, qk_scale, grp, col, slot);
@@ -473,7 +479,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     if (s_pre[mid] <= b0) lo = mid; else hi = mid - 1;
   }
   auto seq_ctx = [&](int s) {
-    int c = a.context_lens[s];
+    int c = read_only(a.context_lens + s);
     return c < cap ? c : cap;
   };
   Cursor cur{lo, b0 - s_pre[lo], s_pre[lo + 1] - s_pre[lo], seq_ctx(lo)};
@@ -542,6 +548,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
       nx = advance(cur);
       if (switch_seq) load_q(qn, a, nx.s, kvh, G, col, grp);
       g_next = geo.load(next, row_of(nx.s), nx.t * kTile, kvh);
+      issue_fence();
       st.tile(now, q, g_now ? cur.ctx - cur.t * kTile : 0, qk_scale, grp, col, slot);
     } else {
       st.tile(now, q, g_now ? cur.ctx - cur.t * kTile : 0, qk_scale, grp, col, slot);

@@ -102,84 +102,80 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of split partials: one 256-thread workgroup per (sequence, head).
-// Every slot with l_p > 0 takes part (a real partial has l_p >= 1: its
-// largest score contributes e^0); unused slots carry l_p = 0. The weights
-// w_p = l_p e^{m_p - M} are computed once per slot (all threads in parallel)
-// and staged in LDS in chunks; each wave then accumulates every 4th used slot
-// over all dims (lane owns dims lane + 64k, coalesced 4-byte rows), and the
-// four waves' sums meet in LDS.
-constexpr int kRedThreads = 256;
-constexpr int kRedChunk = 2048;
+// Merge of split partials: one wave per (sequence, head), four per
+// workgroup, no LDS and no barrier. Every slot with l_p > 0 takes part (a
+// real partial has l_p >= 1: its largest score contributes e^0); unused
+// slots carry l_p = 0. Lanes read the slots' (m, l) 64 at a time; a ballot
+// gives the used ones, whose weights w_p = l_p e^{m_p - M} are broadcast with
+// readlane while every lane accumulates its dims (d = lane + 64k) of o_p.
+constexpr int kRedWaves = 4;
 
-__global__ __launch_bounds__(kRedThreads) void reduce_kernel(
+__global__ __launch_bounds__(kRedWaves * 64) void reduce_kernel(
     float* __restrict__ out, const float* __restrict__ max_logits,
     const float* __restrict__ exp_sums, const float* __restrict__ tmp_out,
-    const int32_t* __restrict__ context_lens, int num_heads, int head_size,
+    const int32_t* __restrict__ context_lens, int num_seqs, int num_heads, int head_size,
     int max_partitions) {
-  __shared__ float s_w[kRedChunk];
-  __shared__ float s_red[kRedThreads / 64];
-  __shared__ float s_acc[kRedThreads / 64][kMaxPerLane * 64];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int h = blockIdx.x;
-  const int seq = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kRedWaves +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (unit >= static_cast<int64_t>(num_seqs) * num_heads) return;
+  const int seq = static_cast<int>(unit / num_heads);
   const int D = head_size;
-  const int64_t orow = static_cast<int64_t>(seq) * num_heads + h;
-  const int n = context_lens[seq] > 0 ? max_partitions : 0;
+  const int64_t orow = unit;  // = seq * num_heads + h
+  const int n = read_only(context_lens + seq) > 0 ? max_partitions : 0;
   const float* __restrict__ m = max_logits + orow * max_partitions;
   const float* __restrict__ l = exp_sums + orow * max_partitions;
   const float* __restrict__ o = tmp_out + orow * max_partitions * D;
 
   float mx = -INFINITY;
-  for (int p = tid; p < n; p += kRedThreads)
+  for (int p = lane; p < n; p += 64)
     if (l[p] > 0.f) mx = fmaxf(mx, m[p]);
-  mx = wave_max(mx);
-  if (lane == 0) s_red[w] = mx;
-  __syncthreads();
-  float M = s_red[0];
-#pragma unroll
-  for (int i = 1; i < kRedThreads / 64; ++i) M = fmaxf(M, s_red[i]);
+  const float M = wave_max(mx);
 
   float acc[kMaxPerLane] = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int c0 = 0; c0 < n; c0 += kRedChunk) {
-    const int cn = n - c0 < kRedChunk ? n - c0 : kRedChunk;
-    __syncthreads();  // previous chunk's weights are no longer read
-    for (int p = tid; p < cn; p += kRedThreads) {
-      const float lp = l[c0 + p];
-      const float wp = lp > 0.f ? lp * expf(m[c0 + p] - M) : 0.f;
-      s_w[p] = wp;
-      den += wp;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int p = c0 + lane;
+    float wp = 0.f;
+    if (p < n) {
+      const float lp = l[p];
+      wp = lp > 0.f ? lp * expf(m[p] - M) : 0.f;
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int p = w; p < cn; p += kRedThreads / 64) {
-      const float wp = s_w[p];
-      if (wp == 0.f) continue;  // unused slot: its row is never read
-      const float* __restrict__ row = o + static_cast<int64_t>(c0 + p) * D;
+    den += wp;
+    uint64_t used = __ballot(wp != 0.f);
+    // four used slots per round, so four rows are in flight at once
+    while (used) {
+      int b[4];
+      float wb[4];
 #pragma unroll
-      for (int k = 0; k < kMaxPerLane; ++k) {
-        const int d = lane + 64 * k;
-        if (d < D) acc[k] = fmaf(wp, row[d], acc[k]);
+      for (int u = 0; u < 4; ++u) {
+        b[u] = used ? __builtin_ctzll(used) : -1;
+        used &= used ? used - 1 : 0;
+        wb[u] = b[u] < 0 ? 0.f
+                         : __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                         __builtin_bit_cast(int, wp), b[u]));
       }
+      float v[4][kMaxPerLane];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float* __restrict__ row = o + static_cast<int64_t>(c0 + (b[u] < 0 ? 0 : b[u])) * D;
+#pragma unroll
+        for (int k = 0; k < kMaxPerLane; ++k) {
+          const int d = lane + 64 * k;
+          v[u][k] = (b[u] >= 0 && d < D) ? row[d] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < kMaxPerLane; ++k) acc[k] = fmaf(wb[u], v[u][k], acc[k]);
     }
   }
   den = wave_sum(den);
-  __syncthreads();
-  if (lane == 0) s_red[w] = den;
 #pragma unroll
-  for (int k = 0; k < kMaxPerLane; ++k) s_acc[w][lane + 64 * k] = acc[k];
-  __syncthreads();
-  float total = 0.f;
-#pragma unroll
-  for (int i = 0; i < kRedThreads / 64; ++i) total += s_red[i];
-  for (int d = tid; d < D; d += kRedThreads) {
-    float num = 0.f;
-#pragma unroll
-    for (int i = 0; i < kRedThreads / 64; ++i) num += s_acc[i][d];
-    out[orow * D + d] = (n > 0 && total > 0.f) ? num / total : 0.f;
+  for (int k = 0; k < kMaxPerLane; ++k) {
+    const int d = lane + 64 * k;
+    if (d < D) out[orow * D + d] = (n > 0 && den > 0.f) ? acc[k] / den : 0.f;
   }
 }
 
@@ -200,10 +196,12 @@ hipError_t launch_reduce(float* out, const float* max_logits, const float* exp_s
                          const float* tmp_out, const int32_t* context_lens, int num_seqs,
                          int num_heads, int head_size, int partition_size, int max_partitions,
                          hipStream_t stream) {
-  dim3 grid(num_heads, num_seqs);
   (void)partition_size;
-  reduce_kernel<<<grid, kRedThreads, 0, stream>>>(out, max_logits, exp_sums, tmp_out, context_lens,
-                                                  num_heads, head_size, max_partitions);
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_heads;
+  const unsigned blocks = static_cast<unsigned>((units + kRedWaves - 1) / kRedWaves);
+  reduce_kernel<<<blocks, kRedWaves * 64, 0, stream>>>(out, max_logits, exp_sums, tmp_out,
+                                                       context_lens, num_seqs, num_heads,
+                                                       head_size, max_partitions);
   return hipGetLastError();
 }
 

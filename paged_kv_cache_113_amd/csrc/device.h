@@ -40,6 +40,15 @@ __device__ __forceinline__ float hi_f16(uint32_t w) {
   return static_cast<float>(h);
 }
 
+// Loads of data the kernels only read (block tables, lengths) go through the
+// constant address space: with a uniform address they become scalar loads,
+// which do not wait behind the vector loads of K/V tiles in flight.
+template <typename T>
+__device__ __forceinline__ T read_only(const T* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) T*>(
+      reinterpret_cast<uintptr_t>(p));
+}
+
 // Physical block of logical position `pos`, or -1 when the table row does not
 // cover it or holds an id outside [0, num_blocks). Callers skip such
 // positions, so a bad table never turns into an out-of-bounds access.
@@ -48,7 +57,7 @@ __device__ __forceinline__ int64_t physical_block(const int32_t* table_row, int 
                                                   int64_t num_blocks) {
   int lb = pos / block_size;
   if (pos < 0 || lb >= max_blocks) return -1;
-  int64_t b = table_row[lb];
+  int64_t b = read_only(table_row + lb);
   return (b >= 0 && b < num_blocks) ? b : -1;
 }
 

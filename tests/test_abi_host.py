@@ -98,7 +98,7 @@ def test_reduce_validation(lib):
     assert f(None, P, P, P, P, 2, 8, 128, 512, 4, None) == ENULL
     assert f(P, P, None, P, P, 2, 8, 128, 512, 4, None) == ENULL
     assert f(P, P, P, P, P, 0, 8, 128, 512, 4, None) == OK
-    assert f(P, P, P, P, P, 70000, 8, 128, 512, 4, None) == EUNSUP
+    assert f(P, P, P, P, P, 1 << 30, 64, 128, 512, 4, None) == EUNSUP   # grid too large
 
 
 def test_write_validation(lib):
