@@ -240,15 +240,21 @@ def main():
         torch.cuda.synchronize()
         total_s = time.perf_counter() - t_start
     else:
-        # single-layer workloads: evict L2/MALL before each step (not timed)
+        # single-layer workloads: evict L2/MALL before each step. The
+        # evicting read is enqueued first and the step's own events are
+        # recorded behind it, so the step's launches are already queued when
+        # the GPU reaches them and the step time is device time, free of the
+        # host's launch latency
         total_s = 0.0
         for _ in range(args.steps):
             flush.sum()
-            torch.cuda.synchronize()
-            t1 = time.perf_counter()
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record()
             step(("decode",))
+            s1.record()
             torch.cuda.synchronize()
-            total_s += time.perf_counter() - t1
+            total_s += s0.elapsed_time(s1) / 1e3
     ms_per_step = total_s / args.steps * 1e3
     # the smaller kernels' own durations, from one more (untimed) step
     step(("write", "reduce"))

@@ -29,9 +29,10 @@
  * new K/V alike. Arithmetic is float32 throughout (scores, softmax, sums).
  *
  * Ownership and threading: the caller allocates and owns every buffer. The
- * library allocates nothing, keeps no pointer after a call returns, has no
- * mutable global state (calls are reentrant) and never synchronises: each
- * call validates its arguments on the host, then enqueues kernels on
+ * library allocates nothing and keeps no pointer after a call returns. Its
+ * only global state is a write-once, per-device cache of one occupancy query
+ * (atomics; calls are reentrant and thread-safe). It never synchronises:
+ * each call validates its arguments on the host, then enqueues kernels on
  * `stream` (a hipStream_t passed as void*; NULL is the default stream) and
  * returns. Device faults surface at the caller's next synchronisation.
  *

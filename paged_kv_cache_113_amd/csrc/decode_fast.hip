@@ -31,8 +31,8 @@
 //    significant bits.
 //  * V: lane (dim chunk c = lane%16, group j) loads 16 B of rows 4j + i
 //    (i = 0..3), 4 rows x 256 contiguous bytes per load, and stores them in
-//    the wave's 4 KiB LDS slot (32-byte chunks XOR-swizzled by row against
-//    bank conflicts). ds_read_b64_tr_b16 then hands lane (d, j) the four
+//    the wave's LDS slot (rows padded to 288 B against bank conflicts).
+//    ds_read_b64_tr_b16 then hands lane (d, j) the four
 //    positions 4j..4j+3 of dim 16*db + d: the A operand (V^T) of the P.V
 //    product, eight blocks db per tile, accumulated in fp32 as O^T[d][n].
 //
@@ -47,6 +47,7 @@
 //    sequence or its range ends. Waves with the same range and different KV
 //    heads run side by side, so the KV heads of a physical block (contiguous
 //    in the pool) are read at about the same time.
+#include <atomic>
 #include <type_traits>
 
 #include "device.h"
@@ -60,7 +61,12 @@ constexpr int kTile = 16;         // positions per tile
 constexpr int kWavesUnsplit = 4;  // waves per (sequence, KV head) without a split
 constexpr int kSplitThreads = 256;
 constexpr int kMaxSeqsBalanced = 8192;  // LDS prefix capacity of the split kernel
-constexpr int kSlotBytes = kTile * kD * 2;  // one wave's V tile in LDS (4 KiB)
+constexpr int kXcds = 8;                // MI355X: 8 XCDs of 32 CUs
+// One wave's V tile in LDS: 16 rows of 256 B, each padded to 288 B so that
+// the 16 rows of a transpose read start 8 banks apart (a 2-way pattern, the
+// minimum for 512 B) and every access is a lane base plus an immediate.
+constexpr int kSlotRow = kD * 2 + 32;
+constexpr int kSlotBytes = kTile * kSlotRow;
 
 #define PKV_LDS __attribute__((address_space(3)))
 
@@ -198,12 +204,6 @@ __device__ __forceinline__ void load_q(uint4* q, const DecodeArgs& a, int seq, i
                     : make_uint4(0, 0, 0, 0);
 }
 
-// Byte offset, in a V slot, of 16-byte chunk `chunk` (0..15) of row `row`:
-// rows are 256 B; the 32-byte chunk index is XORed with row % 8.
-__device__ __forceinline__ int slot_offset(int row, int chunk) {
-  return row * (kD * 2) + (((chunk >> 1) ^ (row & 7)) << 5) + ((chunk & 1) << 4);
-}
-
 // Running softmax state of one wave: lane (col n, group j) keeps column n's
 // running max and its partial sum over rows 4j..4j+3, and acc[db][r] =
 // O^T[16*db + 4j + r][n] (unnormalised), for the G (<= 16) heads of a KV head.
@@ -242,27 +242,26 @@ struct Attend {
     l_part = l_part * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
 
     // V rows into LDS; on the tail tile masked rows become zeros (P is 0
-    // there, and 0 * NaN would still be NaN)
+    // there, and 0 * NaN would still be NaN). Lane (chunk c, group j) holds
+    // 16 B of rows 4j + i.
+    PKV_LDS char* wbase = slot + (4 * grp) * kSlotRow + col * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint4 v = t.v[i];
       if (lim < kTile && 4 * grp + i >= lim) v = make_uint4(0, 0, 0, 0);
-      *(PKV_LDS u32x4*)(slot + slot_offset(4 * grp + i, col)) = __builtin_bit_cast(u32x4, v);
+      *(PKV_LDS u32x4*)(wbase + i * kSlotRow) = __builtin_bit_cast(u32x4, v);
     }
     uint2 phi, plo;
     split_p<T>(p, phi, plo);
-    if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int db = 0; db < 8; ++db) acc[db] *= alpha;
-    }
+    for (int db = 0; db < 8; ++db) acc[db] *= alpha;
     // lane (d = col, group j): positions 4j..4j+3 of dim 16*db + d, gathered by
-    // the transpose read from rows 4j + col/4, bytes 8*(col%4) of chunk db
-    const int rrow = 4 * grp + (col >> 2);
+    // the transpose read from row 4j + col/4, bytes 32*db + 8*(col%4)
+    PKV_LDS char* rbase = slot + (4 * grp + (col >> 2)) * kSlotRow + (col & 3) * 8;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const int off = rrow * (kD * 2) + ((db ^ (rrow & 7)) << 5) + ((col & 3) << 3);
       const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (PKV_LDS s16x4*)(slot + off));
+          (PKV_LDS s16x4*)(rbase + 32 * db));
       const uint2 a = __builtin_bit_cast(uint2, vt);
       acc[db] = mfma_k16<T>(a, phi, acc[db]);
       acc[db] = mfma_k16<T>(a, plo, acc[db]);
@@ -448,10 +447,17 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   __syncthreads();
   if (T1 == 0) return;
 
-  // 2. this wave's KV head and range of the stream. Ranges hold at least
-  //    q_min tiles so that no sequence is cut into more than max_partitions
-  //    pieces: a sequence of n tiles meets at most ceil((n-1)/q_min) + 1.
-  const int gw = blockIdx.x * (kSplitThreads / 64) + w;
+  // 2. this wave's KV head and range of the stream. Workgroups are dealt to
+  //    the 8 XCDs round-robin (workgroup i runs on XCD i % 8); numbering the
+  //    waves XCD by XCD gives each XCD a contiguous run of ranges over all KV
+  //    heads, so the heads of a block are read side by side on one XCD.
+  //    Ranges hold at least q_min tiles so that no sequence is cut into more
+  //    than max_partitions pieces: a sequence of n tiles meets at most
+  //    ceil((n-1)/q_min) + 1.
+  const int n_wg = gridDim.x;
+  const int xcd_rank = (blockIdx.x % kXcds) * (n_wg / kXcds) + blockIdx.x / kXcds;
+  const int wg_rank = n_wg % kXcds == 0 ? xcd_rank : static_cast<int>(blockIdx.x);
+  const int gw = wg_rank * (kSplitThreads / 64) + w;
   const int kvh = gw % a.num_kv_heads;
   const int k = gw / a.num_kv_heads;
   int64_t Wk = waves_per_kv;
@@ -472,24 +478,27 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     return static_cast<int>(((static_cast<int64_t>(x) + 1) * Wk - 1) / T1);
   };
 
+  // LDS reads come back in VGPRs; the prefix is the same for every lane, and
+  // saying so keeps the cursor, table reads and tile addresses scalar
+  auto pre = [&](int s) { return __builtin_amdgcn_readfirstlane(s_pre[s]); };
   // sequence holding tile b0: largest s with s_pre[s] <= b0
   int lo = 0, hi = S - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (s_pre[mid] <= b0) lo = mid; else hi = mid - 1;
+    if (pre(mid) <= b0) lo = mid; else hi = mid - 1;
   }
   auto seq_ctx = [&](int s) {
     int c = read_only(a.context_lens + s);
     return c < cap ? c : cap;
   };
-  Cursor cur{lo, b0 - s_pre[lo], s_pre[lo + 1] - s_pre[lo], seq_ctx(lo)};
-  int piece = k - range_of(s_pre[lo]);  // index of this wave's piece of cur.s
+  Cursor cur{lo, b0 - pre(lo), pre(lo + 1) - pre(lo), seq_ctx(lo)};
+  int piece = k - range_of(pre(lo));  // index of this wave's piece of cur.s
 
   auto advance = [&](const Cursor& c) {
     if (c.t + 1 < c.n) return Cursor{c.s, c.t + 1, c.n, c.ctx};
     int s = c.s + 1;
-    while (s < S - 1 && s_pre[s + 1] == s_pre[s]) ++s;  // sequences with no positions
-    return Cursor{s, 0, s_pre[s + 1] - s_pre[s], seq_ctx(s)};
+    while (s < S - 1 && pre(s + 1) == pre(s)) ++s;  // sequences with no positions
+    return Cursor{s, 0, pre(s + 1) - pre(s), seq_ctx(s)};
   };
   auto row_of = [&](int s) { return a.block_table + static_cast<int64_t>(s) * a.max_blocks; };
 
@@ -568,17 +577,53 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   }
 }
 
+// Resident workgroups of the split kernel on one device, for a given
+// dynamic LDS size class. Computed on first use and kept: the answer only
+// depends on the device and the kernel, and the query costs host time that
+// would otherwise sit between back-to-back launches.
+constexpr int kMaxDevices = 64;
+constexpr int kLdsClasses = 4;  // prefix sizes up to 2, 8, 16, 33 KiB
+
+inline int lds_class(size_t dyn) {
+  return dyn <= 2048 ? 0 : dyn <= 8192 ? 1 : dyn <= 16384 ? 2 : 3;
+}
+inline size_t lds_class_bytes(int c) {
+  const size_t b[kLdsClasses] = {2048, 8192, 16384, (kMaxSeqsBalanced + 1) * sizeof(int)};
+  return b[c];
+}
+
+template <typename T>
+hipError_t split_grid(int& cus, int& per_cu, size_t dyn) {
+  static std::atomic<int> cache[kMaxDevices][kLdsClasses][2];  // 0 = not computed yet
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const int c = lds_class(dyn);
+  if (dev >= 0 && dev < kMaxDevices) {
+    cus = cache[dev][c][0].load(std::memory_order_relaxed);
+    per_cu = cache[dev][c][1].load(std::memory_order_relaxed);
+    if (cus > 0 && per_cu > 0) return hipSuccess;
+  }
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<T>,
+                                                     kSplitThreads, lds_class_bytes(c));
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) per_cu = 1;
+  if (dev >= 0 && dev < kMaxDevices) {
+    cache[dev][c][1].store(per_cu, std::memory_order_relaxed);
+    cache[dev][c][0].store(cus, std::memory_order_relaxed);
+  }
+  return hipSuccess;
+}
+
 template <typename T>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
   auto kernel = decode_split_kernel<T>;
   const size_t dyn = static_cast<size_t>(a.num_seqs + 1) * sizeof(int);
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kSplitThreads, dyn);
+  int cus = 0, per_cu = 0;
+  hipError_t e = split_grid<T>(cus, per_cu, dyn);
   if (e != hipSuccess) return e;
-  if (per_cu < 1) per_cu = 1;
   const int waves_per_wg = kSplitThreads / 64;
   // whole groups of num_kv_heads waves, no more than the GPU holds at once
   int64_t waves = static_cast<int64_t>(cus) * per_cu * waves_per_wg;
