@@ -3,7 +3,7 @@
 Default workload: the full decode step -- 512 sequences, cached lengths
 U{64..4096}, 32 layers, bf16, Hq=32, Hkv=8, D=128, block 16. One step = one
 slot-mapping launch for the batch, then for every layer: the new tokens' K/V
-write, split decode attention (balanced pieces, 256-position slots) and the
+write, split decode attention (balanced pieces, 1024-position slots) and the
 log-sum-exp merge. Inputs are resident in HBM before timing starts.
 
 Prints one JSON line. `value` is KV-read GB/s over the whole step: the
@@ -45,7 +45,7 @@ def kernel_source_hash() -> str:
 def traffic_for(workload: str, kernel_bytes_per_launch: float):
     """HBM bytes per decode launch from the committed rocprofv3 counter
     summary, or None when it is missing or the kernel changed since."""
-    path = os.path.join(ROOT, "profiles", f"decode_fast_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"decode_split_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -68,7 +68,7 @@ def make_batch(workload):
 def default_partition(workload):
     """Split size per workload: it sizes the partial slots (max_partitions =
     ceil(max ctx / P)); smaller P leaves the balanced split more freedom."""
-    return {"decode_step_bf16": 256, "long_split_bf16": 1024, "mha_fp16": 256,
+    return {"decode_step_bf16": 1024, "long_split_bf16": 1024, "mha_fp16": 256,
             "gqa_shared_bf16": 1024, "tiny": 0}[workload]
 
 
