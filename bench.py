@@ -60,9 +60,11 @@ def kv_bytes(batch, lens) -> float:
     return float(np.sum(lens, dtype=np.int64)) * 2 * batch.num_kv_heads * batch.head_size * e
 
 
-def make_batch(workload):
+def make_batch(workload, block_size=None):
     import workloads as W
-    return W.CASES[workload]()
+    if block_size is None:
+        return W.CASES[workload]()
+    return W.CASES[workload](block_size=block_size)
 
 
 def default_partition(workload):
@@ -129,6 +131,9 @@ def main():
                              "long_split_bf16"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="decode step only (default 32)")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="positions per physical block (block-size study; the workloads "
+                         "define 16, or 32 for the long split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -148,7 +153,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    batch = make_batch(args.workload)
+    batch = make_batch(args.workload, args.block_size)
     if args.layers is not None:
         batch.num_layers = args.layers
     L = batch.num_layers

@@ -167,19 +167,22 @@ def _uniform_case(name, dtype, hq, hkv, d, b, num_seqs, lo, hi, seed, partition_
                  partition_size=partition_size)
 
 
-def mha_fp16(num_seqs: int = 64, lo: int = 128, hi: int = 2048, seed: int = 1002) -> Batch:
+def mha_fp16(num_seqs: int = 64, lo: int = 128, hi: int = 2048, seed: int = 1002,
+             block_size: int = 16) -> Batch:
     """Single-layer MHA decode, fp16, Hq=Hkv=32, D=128, B=16, lengths U{lo..hi}."""
-    return _uniform_case("mha_fp16", "f16", 32, 32, 128, 16, num_seqs, lo, hi, seed)
+    return _uniform_case("mha_fp16", "f16", 32, 32, 128, block_size, num_seqs, lo, hi, seed)
 
 
 def gqa_shared_bf16(num_seqs: int = 256, median: float = 1024.0, clip=(16, 8192),
                     sigma: float = 1.0, share_frac: float = 0.3, prefix_blocks: int = 32,
-                    seed: int = 1003) -> Batch:
+                    seed: int = 1003, block_size: int = 16) -> Batch:
     """Single-layer GQA decode with prefix sharing, bf16, Hq=32, Hkv=8, D=128,
     B=16; lengths clip(rint(median * exp(sigma * Z)), clip); round(share_frac *
     S) sequences whose length covers the prefix map their first
-    ``prefix_blocks`` logical blocks to the same physical blocks."""
-    b = 16
+    ``prefix_blocks`` logical blocks to the same physical blocks. Another
+    block size keeps the shared prefix at the same number of positions."""
+    b = block_size
+    prefix_blocks = max(1, prefix_blocks * 16 // b)
     rng = np.random.default_rng(seed)
     z = rng.standard_normal(num_seqs)
     lens = np.clip(np.rint(median * np.exp(sigma * z)), clip[0], clip[1]).astype(np.int64)
@@ -201,21 +204,21 @@ def gqa_shared_bf16(num_seqs: int = 256, median: float = 1024.0, clip=(16, 8192)
 
 
 def long_split_bf16(num_seqs: int = 8, lo: int = 32768, hi: int = 131072,
-                    seed: int = 1004, partition_size: int = 512) -> Batch:
+                    seed: int = 1004, partition_size: int = 512, block_size: int = 32) -> Batch:
     """Long-context split decode, bf16, Hq=64, Hkv=8, D=128, B=32, lengths
     U{lo..hi}, 512-token partitions."""
-    return _uniform_case("long_split_bf16", "bf16", 64, 8, 128, 32, num_seqs, lo, hi, seed,
-                         partition_size=partition_size)
+    return _uniform_case("long_split_bf16", "bf16", 64, 8, 128, block_size, num_seqs, lo, hi,
+                         seed, partition_size=partition_size)
 
 
 def decode_step_bf16(num_seqs: int = 512, lo: int = 64, hi: int = 4096,
-                     num_layers: int = 32, seed: int = 1005) -> Batch:
+                     num_layers: int = 32, seed: int = 1005, block_size: int = 16) -> Batch:
     """Full decode step, bf16, Hq=32, Hkv=8, D=128, B=16: cached lengths
     U{lo..hi}; each sequence grows by its new token (taking a fresh block when
     its cached length is a multiple of 16), ``num_layers`` layers with their
     own pools; tables and positions are shared by all layers."""
-    return _uniform_case("decode_step_bf16", "bf16", 32, 8, 128, 16, num_seqs, lo, hi, seed,
-                         num_layers=num_layers, new_token=True)
+    return _uniform_case("decode_step_bf16", "bf16", 32, 8, 128, block_size, num_seqs, lo, hi,
+                         seed, num_layers=num_layers, new_token=True)
 
 
 CASES = {
