@@ -8,9 +8,10 @@ Parts:
   * ``allocator``   -- FIFO block allocator with refcounts, slot translation,
                        block counting (Python).
   * ``scatter``     -- new-token K/V write, bytewise (numpy).
-  * ``attn_ref.c``  -- gather + fp64 attention, fp64 split partials and their
-                       log-sum-exp merge (plain C, pthreads), loaded here via
-                       ctypes.
+  * ``attn_ref.c``  -- gather + fp64 attention (one query token per sequence,
+                       or several with a causal limit), fp64 split partials
+                       and their log-sum-exp merge (plain C, pthreads),
+                       loaded here via ctypes.
 
 Every function is pinned by tests/test_oracle_*.py against values the pages
 print, closed forms and brute force; none is "parity unpinned".
@@ -63,8 +64,10 @@ def _load():
                                                i32, i32, i64, i32, f32, i32, i32, P,
                                                i32, i32]
         lib.orc_lse_combine.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32]
+        lib.orc_attention_varlen.argtypes = [P, P, P, P, i32, P, P, P, i32, i32, i32, i32,
+                                             i32, i64, i32, f32, i32]
         for f in ("orc_widen", "orc_gather", "orc_attention",
-                  "orc_attention_partials", "orc_lse_combine"):
+                  "orc_attention_partials", "orc_lse_combine", "orc_attention_varlen"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -165,4 +168,26 @@ def lse_combine(m, l, o, ctx_lens, partition_size: int) -> np.ndarray:
     out = np.empty((s, hq, d), dtype=np.float64)
     _check(_load().orc_lse_combine(_ptr(out), _ptr(m), _ptr(l), _ptr(o), _ptr(ctx), s, hq, d,
                                    partition_size, p), "lse_combine")
+    return out
+
+
+def attention_varlen(q, k_pool, v_pool, block_table, query_start_loc, ctx_lens, scale: float,
+                     dtype: str, threads: int = 1) -> np.ndarray:
+    """fp64 attention of multi-token queries: q [num_tokens, Hq, D]; token i
+    of sequence s (tokens qsl[s]..qsl[s+1]-1) attends positions 0 ..
+    ctx_s - q_s + i. Returns [num_tokens, Hq, D]."""
+    qa = _raw(q, dtype)
+    k = _raw(k_pool, dtype)
+    v = _raw(v_pool, dtype)
+    n, hkv, b, d = k.shape
+    nt, hq, _ = qa.shape
+    tab = np.ascontiguousarray(block_table, dtype=np.int32)
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    assert qsl[-1] == nt and len(qsl) == len(ctx) + 1
+    out = np.zeros((nt, hq, d), dtype=np.float64)
+    _check(_load().orc_attention_varlen(_ptr(out), _ptr(qa), _ptr(k), _ptr(v),
+                                        DTYPE_CODES[dtype], _ptr(tab), _ptr(qsl), _ptr(ctx),
+                                        len(ctx), hq, hkv, d, b, n, tab.shape[1], float(scale),
+                                        int(threads)), "attention_varlen")
     return out

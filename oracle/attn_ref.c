@@ -21,6 +21,13 @@
  *    attention is mathematically identical to standard attention). Query head
  *    h reads KV head h / (Hq/Hkv) (glossary page, expand_kv's
  *    repeat_interleave over the KV-head dimension).
+ *  - Multi-token queries (orc_attention_varlen): a sequence brings q_s new
+ *    query tokens at its last q_s positions (chunked prefill, speculative
+ *    decoding; source-walkthrough page, continuous batching, where a step
+ *    mixes prefill chunks and decode tokens, and the vLLM page's attention
+ *    metadata: query start locations and positions). Token i of sequence s
+ *    sits at p = ctx_s - q_s + i and attends positions 0..p (causal): the
+ *    same softmax as above over a prefix of the gathered sequence.
  *  - Split partials (orc_attention_partials) and their log-sum-exp merge
  *    (orc_lse_combine): the pages only say that long sequences are split
  *    into partitions computed in parallel and merged by a reduce kernel
@@ -135,8 +142,10 @@ typedef struct {
   int64_t num_blocks;
   int max_blocks;
   double scale;
-  const int32_t* seqs; /* the sequences to compute, in output order */
+  const int32_t* seqs; /* the sequences to compute, in output order; NULL = all */
   int n_seqs;
+  const int32_t* qsl; /* multi-token queries: [num_seqs + 1] start rows; NULL = one
+                         query token per sequence, query row s */
   int partition_size; /* 0: whole context (orc_attention) */
   int max_partitions;
   /* outputs */
@@ -184,10 +193,16 @@ static void attend_range(const double* qh, const double* K, const double* V, int
 static int run_unit(job_t* j, int64_t unit) {
   int si = (int)(unit / j->hkv);
   int kv = (int)(unit % j->hkv);
-  int s = j->seqs[si];
+  int s = j->seqs ? j->seqs[si] : si;
   int ctx = j->ctx_lens[s];
   int D = j->D, G = j->hq / j->hkv;
-  if (ctx < 0) return ORC_EARG;
+  /* query rows q0 .. q0 + qn - 1 belong to s; row q0 + i is the token at
+   * position ctx - qn + i and sees positions 0 .. ctx - qn + i. One decode
+   * token (qn = 1) sees the whole context. */
+  int q0 = j->qsl ? j->qsl[s] : s;
+  int qn = j->qsl ? j->qsl[s + 1] - j->qsl[s] : 1;
+  int orow = j->qsl ? q0 : si; /* first output row */
+  if (ctx < 0 || qn < 0 || (j->qsl && qn > ctx)) return ORC_EARG;
   double* K = (double*)malloc(sizeof(double) * ((size_t)ctx * D + 1));
   double* V = (double*)malloc(sizeof(double) * ((size_t)ctx * D + 1));
   double* z = (double*)malloc(sizeof(double) * ((size_t)ctx + 1));
@@ -212,25 +227,28 @@ static int run_unit(job_t* j, int64_t unit) {
       V[(int64_t)t * D + d] = widen(j->v_pool, src + d, j->dtype);
     }
   }
-  for (int g = 0; g < G; ++g) {
-    int h = kv * G + g; /* the query heads that read KV head kv */
-    for (int d = 0; d < D; ++d)
-      qh[d] = widen(j->q, ((int64_t)s * j->hq + h) * D + d, j->dtype);
-    if (j->partition_size == 0) {
-      double m, l;
-      attend_range(qh, K, V, 0, ctx, D, j->scale, z, &m, &l, o);
-      double* dst = j->out + ((int64_t)si * j->hq + h) * D;
-      for (int d = 0; d < D; ++d) dst[d] = (ctx > 0) ? o[d] : 0.0;
-    } else {
-      int P = j->partition_size;
-      for (int p = 0; p < j->max_partitions; ++p) {
-        int lo = p * P, hi = (p + 1) * P < ctx ? (p + 1) * P : ctx;
+  for (int i = 0; i < qn; ++i) {
+    int visible = ctx - qn + i + 1; /* causal limit of this query row */
+    for (int g = 0; g < G; ++g) {
+      int h = kv * G + g; /* the query heads that read KV head kv */
+      for (int d = 0; d < D; ++d)
+        qh[d] = widen(j->q, ((int64_t)(q0 + i) * j->hq + h) * D + d, j->dtype);
+      if (j->partition_size == 0) {
         double m, l;
-        attend_range(qh, K, V, lo, hi, D, j->scale, z, &m, &l, o);
-        int64_t idx = ((int64_t)si * j->hq + h) * j->max_partitions + p;
-        j->m_out[idx] = m;
-        j->l_out[idx] = l;
-        for (int d = 0; d < D; ++d) j->o_out[idx * D + d] = o[d];
+        attend_range(qh, K, V, 0, visible, D, j->scale, z, &m, &l, o);
+        double* dst = j->out + ((int64_t)(orow + i) * j->hq + h) * D;
+        for (int d = 0; d < D; ++d) dst[d] = (visible > 0) ? o[d] : 0.0;
+      } else {
+        int P = j->partition_size;
+        for (int p = 0; p < j->max_partitions; ++p) {
+          int lo = p * P, hi = (p + 1) * P < visible ? (p + 1) * P : visible;
+          double m, l;
+          attend_range(qh, K, V, lo, hi, D, j->scale, z, &m, &l, o);
+          int64_t idx = ((int64_t)(orow + i) * j->hq + h) * j->max_partitions + p;
+          j->m_out[idx] = m;
+          j->l_out[idx] = l;
+          for (int d = 0; d < D; ++d) j->o_out[idx * D + d] = o[d];
+        }
       }
     }
   }
@@ -365,4 +383,32 @@ int orc_lse_combine(double* out, const double* m, const double* l, const double*
     }
   }
   return ORC_OK;
+}
+
+/* Multi-token queries (chunked prefill, speculative decoding).
+ * query [num_tokens][hq][D]; query_start_loc [num_seqs + 1], non-decreasing
+ * from 0 (sequence s owns query rows qsl[s] .. qsl[s+1]-1, q_s of them);
+ * ctx_lens [num_seqs] count all positions in the pool, the new tokens'
+ * included, so q_s <= ctx_s. Row qsl[s] + i is the token at position
+ * ctx_s - q_s + i and attends positions 0 .. ctx_s - q_s + i.
+ * out [num_tokens][hq][D]. */
+int orc_attention_varlen(double* out, const void* q, const void* k_pool, const void* v_pool,
+                         int dtype, const int32_t* block_table, const int32_t* query_start_loc,
+                         const int32_t* ctx_lens, int num_seqs, int hq, int hkv, int D, int B,
+                         int64_t num_blocks, int max_blocks, float scale, int threads) {
+  int rc = check_common(hq, hkv, D, B, dtype, num_seqs);
+  if (rc != ORC_OK) return rc;
+  if (!query_start_loc || query_start_loc[0] != 0) return ORC_EARG;
+  for (int s = 0; s < num_seqs; ++s)
+    if (query_start_loc[s + 1] < query_start_loc[s]) return ORC_EARG;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.q = q; j.k_pool = k_pool; j.v_pool = v_pool; j.dtype = dtype;
+  j.block_table = block_table; j.ctx_lens = ctx_lens;
+  j.hq = hq; j.hkv = hkv; j.D = D; j.B = B;
+  j.num_blocks = num_blocks; j.max_blocks = max_blocks;
+  j.scale = (double)scale; j.seqs = NULL; j.n_seqs = num_seqs;
+  j.qsl = query_start_loc;
+  j.partition_size = 0; j.out = out;
+  return run_job(&j, threads);
 }

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import test_oracle_attention as pins
+import test_oracle_varlen as vpins
 
 MUTATIONS = {
     "interleaved head map": ("int h = kv * G + g;", "int h = g * j->hkv + kv;"),
@@ -27,14 +28,20 @@ MUTATIONS = {
     "f16 exponent bias": ("e - 25);", "e - 24);"),
     "bf16 shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
     "K used as V": ("o[d] += w * V[(int64_t)t * D + d];", "o[d] += w * K[(int64_t)t * D + d];"),
-    "partition end": ("(p + 1) * P < ctx ? (p + 1) * P : ctx;",
-                      "(p + 1) * P < ctx ? (p + 1) * P + 1 : ctx;"),
+    "partition end": ("(p + 1) * P < visible ? (p + 1) * P : visible;",
+                      "(p + 1) * P < visible ? (p + 1) * P + 1 : visible;"),
     "merge drops l": ("double w = l[base + p] * exp(m[base + p] - M);",
                       "double w = exp(m[base + p] - M);"),
     "merge sign": ("double w = l[base + p] * exp(m[base + p] - M);",
                    "double w = l[base + p] * exp(M - m[base + p]);"),
-    "q indexed by head first": ("((int64_t)s * j->hq + h) * D + d",
-                                "((int64_t)h * j->hq + s) * D + d"),
+    "q indexed by head first": ("((int64_t)(q0 + i) * j->hq + h) * D + d",
+                                "((int64_t)h * j->hq + (q0 + i)) * D + d"),
+    "causal limit off by one": ("int visible = ctx - qn + i + 1;",
+                                "int visible = ctx - qn + i;"),
+    "causal mask aligned to the start": ("int visible = ctx - qn + i + 1;",
+                                         "int visible = i + 1 < ctx ? i + 1 : ctx;"),
+    "output rows reversed in a chunk": ("j->out + ((int64_t)(orow + i) * j->hq + h) * D;",
+                                        "j->out + ((int64_t)(orow + qn - 1 - i) * j->hq + h) * D;"),
     "max misses first score": ("if (z[t - lo] > m) m = z[t - lo];",
                                "if (t > lo && z[t - lo] > m) m = z[t - lo];"),
 }
@@ -59,6 +66,8 @@ def _run_pins():
         lambda: [pins.test_partials_merge_equals_whole(p) for p in (4, 12)],
         lambda: pins.test_one_token_partitions(),
         lambda: pins.test_lse_combine_closed_forms(),
+        lambda: [vpins.test_varlen_matches_sdpa_lower_right(s) for s in range(4)],
+        lambda: vpins.test_first_prefill_token_sees_one_position(),
     ]
     for c in checks:
         try:
@@ -90,7 +99,7 @@ def test_mutation_is_caught(name, tmp_path, monkeypatch):
     real = oracle._load()
     lib = ctypes.CDLL(so)
     for f in ("orc_widen", "orc_gather", "orc_attention", "orc_attention_partials",
-              "orc_lse_combine"):
+              "orc_lse_combine", "orc_attention_varlen"):
         getattr(lib, f).argtypes = getattr(real, f).argtypes
         getattr(lib, f).restype = ctypes.c_int
     monkeypatch.setattr(oracle, "_lib", lib)
