@@ -179,6 +179,50 @@ int paged_attention_reduce(float* out, const float* max_logits, const float* exp
                            int max_partitions, void* stream);
 
 /*
+ * paged_varlen_attention -- several query tokens per sequence (chunked
+ * prefill, speculative decoding, or a step that mixes them with decode
+ * tokens) over paged KV, with a causal limit inside each sequence.
+ *
+ * A serving step can mix prefill chunks and decode tokens in one batch
+ * (source-walkthrough page, continuous batching; the attention metadata of
+ * "vLLM PagedAttention ...", section 6, carries query start locations and
+ * positions). Sequence s owns query rows query_start_loc[s] ..
+ * query_start_loc[s+1]-1, q_s of them; its new tokens' K/V are already in
+ * the pools (paged_kv_write), so context_lens[s] counts them: q_s <= ctx_s.
+ * Row query_start_loc[s] + i is the token at position p = ctx_s - q_s + i;
+ * for query head h (KV head h / (num_heads/num_kv_heads)) it gets
+ *   out[row][h] = softmax over t <= p of (scale <q, K_s[kv][t]>) applied to V,
+ * with K_s/V_s read through the block table as in paged_decode_attention.
+ * One query token per sequence (q_s = 1) is decode attention.
+ *
+ * query [num_tokens, num_heads, head_size] dtype; query_start_loc
+ * [num_seqs + 1] int32, non-decreasing, from 0 to num_tokens; out
+ * [num_tokens, num_heads, head_size] float32. The call writes `out` itself:
+ * on the matrix-core path it splits each sequence's work over the whole GPU
+ * into pieces (at most max_partitions per query row, so max_partitions >= 8
+ * is a good choice; 1 serialises each KV head), writes their partials into
+ * max_logits/exp_sums [num_tokens, num_heads, max_partitions] and tmp_out
+ * [num_tokens, num_heads, max_partitions, head_size] float32 (size:
+ * paged_attention_workspace_bytes(num_tokens, ...)), and merges them. The
+ * plain path (other shapes) ignores the workspace. Rows no sequence claims
+ * are undefined; rows past a sequence's context (q_s > ctx_s, a caller
+ * error) get 0.
+ *
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_UNSUPPORTED
+ * (head_size > 256, or more than 2^26 (row, head) pairs), PKV_ERR_WORKSPACE
+ * (a NULL workspace pointer), PKV_ERR_LAUNCH. num_seqs == 0 or num_tokens
+ * == 0 is a no-op.
+ */
+int paged_varlen_attention(float* out, const void* query, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* query_start_loc, const int32_t* context_lens,
+                           int num_seqs, int num_tokens, int num_heads, int num_kv_heads,
+                           int head_size, int block_size, int64_t num_blocks,
+                           int max_blocks_per_seq, float scale, int max_partitions,
+                           float* max_logits, float* exp_sums, float* tmp_out, int dtype,
+                           void* stream);
+
+/*
  * paged_attention_workspace_bytes -- bytes of max_logits + exp_sums + tmp_out
  * for a split call: num_seqs * num_heads * max_partitions * (head_size + 2) *
  * 4. Host-only; returns 0 for non-positive arguments.

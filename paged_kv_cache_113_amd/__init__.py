@@ -27,6 +27,9 @@ SIGNATURES = {
     "paged_decode_attention": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                       _I64, _I32, _F32, _I32, _I32, _P, _P, _P, _I32, _P]),
     "paged_attention_reduce": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
+    "paged_varlen_attention": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                      _I32, _I32, _I64, _I32, _F32, _I32, _P, _P, _P, _I32,
+                                      _P]),
     "paged_attention_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "paged_kv_gather": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32,
                                _I32, _I32, _P]),
@@ -122,6 +125,26 @@ def paged_attention_reduce(out, max_logits, exp_sums, tmp_out, context_lens, par
     _check("paged_attention_reduce", lib.paged_attention_reduce(
         _ptr(out), _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out), _ptr(context_lens), s, hq,
         d, partition_size, p, _stream(stream)))
+
+
+def paged_varlen_attention(out, query, k_cache, v_cache, block_table, query_start_loc,
+                           context_lens, scale, max_partitions, max_logits, exp_sums, tmp_out,
+                           stream=None):
+    """Causal attention of several query tokens per sequence (rows
+    query_start_loc[s]..query_start_loc[s+1]-1, at the last positions of the
+    sequence's context) into out [T, Hq, D]; partials go through the
+    workspace [T, Hq, P(, D)]."""
+    _dev(out, query, k_cache, v_cache, block_table, query_start_loc, context_lens, max_logits,
+         exp_sums, tmp_out)
+    assert block_table.dtype == query_start_loc.dtype == context_lens.dtype == torch.int32
+    assert out.dtype == torch.float32
+    n, hkv, b, d = k_cache.shape
+    t, hq, _ = query.shape
+    _check("paged_varlen_attention", lib.paged_varlen_attention(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(query_start_loc), _ptr(context_lens), context_lens.shape[0], t, hq, hkv, d, b, n,
+        block_table.shape[1], float(scale), max_partitions, _ptr(max_logits), _ptr(exp_sums),
+        _ptr(tmp_out), _DTYPE[query.dtype], _stream(stream)))
 
 
 def paged_attention_workspace_bytes(num_seqs, num_heads, head_size, max_partitions):

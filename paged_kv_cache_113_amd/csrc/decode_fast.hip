@@ -220,16 +220,19 @@ struct Attend {
     for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One tile; rows >= lim are masked (their K/V may hold anything, NaN too).
-  // `slot` is this wave's 4 KiB of LDS.
-  __device__ __forceinline__ void tile(const TileRegs& t, const uint4* q, int lim,
+  // One tile. Rows >= slim get no weight in this lane's column (slim may
+  // differ from column to column: a causal limit per query token); V rows
+  // >= vlim (the wave-uniform limit over all columns, >= every slim) are
+  // zeroed, since their K/V may hold anything, NaN too. `slot` is this
+  // wave's 4 KiB of LDS.
+  __device__ __forceinline__ void tile(const TileRegs& t, const uint4* q, int slim, int vlim,
                                        float qk_scale, int grp, int col, PKV_LDS char* slot) {
     f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) S = mfma_k32<T>(t.k[kk], q[kk], S);
     float s[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = (4 * grp + i < lim) ? S[i] * qk_scale : -INFINITY;
+    for (int i = 0; i < 4; ++i) s[i] = (4 * grp + i < slim) ? S[i] * qk_scale : -INFINITY;
     float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mt = max_xor32(max_xor16(mt));
     const float m_new = fmaxf(m_run, mt);
@@ -248,7 +251,7 @@ struct Attend {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint4 v = t.v[i];
-      if (lim < kTile && 4 * grp + i >= lim) v = make_uint4(0, 0, 0, 0);
+      if (vlim < kTile && 4 * grp + i >= vlim) v = make_uint4(0, 0, 0, 0);
       *(PKV_LDS u32x4*)(wbase + i * kSlotRow) = __builtin_bit_cast(u32x4, v);
     }
     uint2 phi, plo;
@@ -323,16 +326,18 @@ __global__ __launch_bounds__(kWavesUnsplit * 64) void decode_whole_kernel(Decode
   for (; ti + 1 < my_n; ti += 2) {
     gb = geo.load(tb, row, tok(ti + 1), kvh);
     issue_fence();
-    st.tile(ta, q, ga ? ctx - tok(ti) : 0, qk_scale, grp, col, slot);
+    st.tile(ta, q, ga ? ctx - tok(ti) : 0, ga ? ctx - tok(ti) : 0, qk_scale, grp, col, slot);
     if (ti + 2 < my_n) {
       ga = geo.load(ta, row, tok(ti + 2), kvh);
       issue_fence();
-      st.tile(tb, q, gb ? ctx - tok(ti + 1) : 0, qk_scale, grp, col, slot);
+      st.tile(tb, q, gb ? ctx - tok(ti + 1) : 0, gb ? ctx - tok(ti + 1) : 0, qk_scale, grp,
+              col, slot);
     } else {
-      st.tile(tb, q, gb ? ctx - tok(ti + 1) : 0, qk_scale, grp, col, slot);
+      st.tile(tb, q, gb ? ctx - tok(ti + 1) : 0, gb ? ctx - tok(ti + 1) : 0, qk_scale, grp,
+              col, slot);
     }
   }
-  if (ti < my_n) st.tile(ta, q, ga ? ctx - tok(ti) : 0, qk_scale, grp, col, slot);
+  if (ti < my_n) st.tile(ta, q, ga ? ctx - tok(ti) : 0, ga ? ctx - tok(ti) : 0, qk_scale, grp, col, slot);
   const float l_col = st.column_sum();
 
   __syncthreads();  // every wave is done with its V slot
@@ -369,12 +374,32 @@ __global__ __launch_bounds__(kWavesUnsplit * 64) void decode_whole_kernel(Decode
 // split: persistent, balanced over tiles
 // ---------------------------------------------------------------------------
 
-// A tile of the per-KV-head stream: sequence s, tile t of its n tiles.
+// Stream units. Decode: one unit per sequence, its single query token in
+// columns 0..G-1. Multi-token queries (kVar): a sequence's q_s tokens are cut
+// into column groups of tpg = 16 / G tokens; column n of group c is token
+// c*tpg + n / G, query head kv*G + n % G. Token i of a sequence with ctx
+// positions sits at position ctx - q_s + i and sees positions 0 .. ctx - q_s + i
+// (causal); a group's tiles cover what its last token sees, and each group
+// re-reads the sequence's K/V from position 0.
+//
+// Tiles of group c: ceil(visible of its last token / 16), at least one, so
+// that every query row gets a partial (a fully masked tile when a token sees
+// nothing, which only malformed metadata produces).
+__device__ __forceinline__ int group_tiles(int ctx, int qn, int c, int tpg) {
+  const int e = (c + 1) * tpg < qn ? (c + 1) * tpg : qn;
+  const int vis = ctx - qn + e;
+  const int n = vis > 0 ? (vis + kTile - 1) / kTile : 0;
+  return n > 0 ? n : 1;
+}
+
+// A tile of the per-KV-head stream: tile t of the n tiles of unit (s, c).
 struct Cursor {
   int s, t, n, ctx;
+  int c, nu;   // column group and groups of s (kVar; 0 and 1 for decode)
+  int q0, qn;  // first query row of s and its query tokens (kVar)
 };
 
-template <typename T>
+template <typename T, bool kVar>
 __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs a,
                                                                      int waves_per_kv) {
   extern __shared__ int s_pre[];  // [S + 1]: tiles before sequence s
@@ -390,6 +415,45 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   const int G = a.num_heads / a.num_kv_heads;
   const int mp = a.max_partitions;
   const int cap = a.max_blocks * a.block_size;
+  const int tpg = kVar ? kTile / G : 1;  // query tokens per column group
+
+  auto seq_ctx = [&](int s) {
+    int c = read_only(a.context_lens + s);
+    return c < cap ? c : cap;
+  };
+  // query rows of sequence s, clamped to [0, num_tokens]
+  auto seq_rows = [&](int s, int& q0, int& qn) {
+    if constexpr (kVar) {
+      int lo = read_only(a.query_start_loc + s);
+      int hi = read_only(a.query_start_loc + s + 1);
+      lo = lo < 0 ? 0 : (lo > a.num_tokens ? a.num_tokens : lo);
+      hi = hi < lo ? lo : (hi > a.num_tokens ? a.num_tokens : hi);
+      q0 = lo;
+      qn = hi - lo;
+    } else {
+      q0 = s;
+      qn = 1;
+    }
+  };
+  auto groups_of = [&](int qn) { return kVar ? (qn + tpg - 1) / tpg : 1; };
+  auto unit_tiles = [&](int ctx, int qn, int c) {
+    if constexpr (kVar) return group_tiles(ctx, qn, c, tpg);
+    return ctx > 0 ? (ctx + kTile - 1) / kTile : 0;
+  };
+  // tiles of all units of sequence s, and of its largest (last) unit
+  auto seq_tiles = [&](int s, int& last) {
+    const int ctx = seq_ctx(s);
+    int q0, qn;
+    seq_rows(s, q0, qn);
+    const int nu = groups_of(qn);
+    int tot = 0;
+    last = 0;
+    for (int c = 0; c < nu; ++c) {
+      last = unit_tiles(ctx, qn, c);
+      tot += last;
+    }
+    return tot;
+  };
 
   // 1. tiles per sequence and their exclusive prefix (every workgroup builds
   //    the same table; it is tiny next to the KV stream)
@@ -399,11 +463,9 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   for (int i = 0; i < per; ++i) {
     const int s = s_lo + i;
     if (s < S) {
-      int c = a.context_lens[s];
-      c = c < cap ? c : cap;
-      const int nt = c > 0 ? (c + kTile - 1) / kTile : 0;
-      local += nt;
-      nmax = nt > nmax ? nt : nmax;
+      int last;
+      local += seq_tiles(s, last);
+      nmax = last > nmax ? last : nmax;
     }
   }
   int incl = local;  // inclusive scan over the wave
@@ -437,9 +499,8 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
       const int s = s_lo + i;
       if (s < S) {
         s_pre[s] = run;
-        int c = a.context_lens[s];
-        c = c < cap ? c : cap;
-        run += c > 0 ? (c + kTile - 1) / kTile : 0;
+        int last;
+        run += seq_tiles(s, last);
       }
     }
     if (tid == 0) s_pre[S] = T1;
@@ -451,8 +512,8 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   //    the 8 XCDs round-robin (workgroup i runs on XCD i % 8); numbering the
   //    waves XCD by XCD gives each XCD a contiguous run of ranges over all KV
   //    heads, so the heads of a block are read side by side on one XCD.
-  //    Ranges hold at least q_min tiles so that no sequence is cut into more
-  //    than max_partitions pieces: a sequence of n tiles meets at most
+  //    Ranges hold at least q_min tiles so that no unit is cut into more
+  //    than max_partitions pieces: a unit of n tiles meets at most
   //    ceil((n-1)/q_min) + 1.
   const int n_wg = gridDim.x;
   const int xcd_rank = (blockIdx.x % kXcds) * (n_wg / kXcds) + blockIdx.x / kXcds;
@@ -487,52 +548,126 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     const int mid = (lo + hi + 1) >> 1;
     if (pre(mid) <= b0) lo = mid; else hi = mid - 1;
   }
-  auto seq_ctx = [&](int s) {
-    int c = read_only(a.context_lens + s);
-    return c < cap ? c : cap;
+  auto open_seq = [&](int s) {
+    Cursor c;
+    c.s = s;
+    c.t = 0;
+    c.c = 0;
+    c.ctx = seq_ctx(s);
+    seq_rows(s, c.q0, c.qn);
+    c.nu = groups_of(c.qn);
+    c.n = unit_tiles(c.ctx, c.qn, 0);
+    return c;
   };
-  Cursor cur{lo, b0 - pre(lo), pre(lo + 1) - pre(lo), seq_ctx(lo)};
-  int piece = k - range_of(pre(lo));  // index of this wave's piece of cur.s
+  Cursor cur = open_seq(lo);
+  int ustart = pre(lo);  // stream index of the first tile of cur's unit
+  {
+    int x = b0 - ustart;
+    if constexpr (kVar) {
+      while (x >= cur.n && cur.c + 1 < cur.nu) {
+        x -= cur.n;
+        ustart += cur.n;
+        ++cur.c;
+        cur.n = unit_tiles(cur.ctx, cur.qn, cur.c);
+      }
+    }
+    cur.t = x;
+  }
+  int piece = k - range_of(ustart);  // index of this wave's piece of the unit
 
   auto advance = [&](const Cursor& c) {
-    if (c.t + 1 < c.n) return Cursor{c.s, c.t + 1, c.n, c.ctx};
+    Cursor r = c;
+    if (c.t + 1 < c.n) {
+      r.t = c.t + 1;
+      return r;
+    }
+    if (kVar && c.c + 1 < c.nu) {
+      r.c = c.c + 1;
+      r.t = 0;
+      r.n = unit_tiles(c.ctx, c.qn, r.c);
+      return r;
+    }
     int s = c.s + 1;
-    while (s < S - 1 && pre(s + 1) == pre(s)) ++s;  // sequences with no positions
-    return Cursor{s, 0, pre(s + 1) - pre(s), seq_ctx(s)};
+    while (s < S - 1 && pre(s + 1) == pre(s)) ++s;  // sequences with no tiles
+    return open_seq(s);
   };
   auto row_of = [&](int s) { return a.block_table + static_cast<int64_t>(s) * a.max_blocks; };
+
+  // this lane's column: token offset within its group and head within the
+  // KV head's group of query heads
+  const int my_tok = kVar ? col / G : 0;
+  const int my_g = kVar ? col % G : col;
+  const bool my_col = kVar ? col < tpg * G : col < G;
+  auto lane_token = [&](const Cursor& c) { return c.c * tpg + my_tok; };
+  auto lane_live = [&](const Cursor& c) { return my_col && lane_token(c) < c.qn; };
 
   const Geo geo(a, col, grp);
   const float qk_scale = a.scale * kLog2e;
   PKV_LDS char* slot = (PKV_LDS char*)(s_slots) + w * kSlotBytes;
+
+  // Q^T operand of a unit: lane (col n, group j) holds its column's query at
+  // dim chunks 4*kk + j; zero for unused columns.
+  auto load_q_unit = [&](uint4* qq, const Cursor& c) {
+    if constexpr (kVar) {
+      const bool ok = lane_live(c);
+      const char* qp = static_cast<const char*>(a.query) +
+                       ((static_cast<int64_t>(c.q0 + lane_token(c)) * a.num_heads + kvh * G +
+                         my_g) * kD) * 2;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qq[kk] = ok ? *reinterpret_cast<const uint4*>(qp + (4 * kk + grp) * 16)
+                    : make_uint4(0, 0, 0, 0);
+    } else {
+      load_q(qq, a, c.s, kvh, G, col, grp);
+    }
+  };
+  // score limit of this lane's column and the wave-uniform V limit, relative
+  // to the first position of tile c.t
+  auto limits = [&](const Cursor& c, bool g_ok, int& slim, int& vlim) {
+    const int tok0 = c.t * kTile;
+    if (!g_ok) {
+      slim = vlim = 0;
+      return;
+    }
+    if constexpr (kVar) {
+      const int e = (c.c + 1) * tpg < c.qn ? (c.c + 1) * tpg : c.qn;
+      vlim = c.ctx - c.qn + e - tok0;
+      slim = lane_live(c) ? c.ctx - c.qn + lane_token(c) + 1 - tok0 : 0;
+    } else {
+      slim = vlim = c.ctx - tok0;
+    }
+  };
+
   uint4 q[4], qn[4];
-  load_q(q, a, cur.s, kvh, G, col, grp);
+  load_q_unit(q, cur);
   Attend<T> st;
   st.reset();
 
-  // write this piece's partial; after a sequence's last piece, mark the
-  // remaining slots unused (l = 0) so the merge skips them
+  // write this piece's partial; after a unit's last piece, mark the remaining
+  // slots unused (l = 0) so the merge skips them
   auto finish = [&](const Cursor& c) {
     const float l_col = st.column_sum();
-    const int64_t row0 = static_cast<int64_t>(c.s) * a.num_heads + kvh * G;
-    if (col < G) {
+    const int64_t prow = kVar ? static_cast<int64_t>(c.q0 + lane_token(c)) * a.num_heads +
+                                    kvh * G + my_g
+                              : static_cast<int64_t>(c.s) * a.num_heads + kvh * G + col;
+    if (kVar ? lane_live(c) : my_col) {
       if (piece < mp) {
         const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
-        float* dst = a.tmp_out + ((row0 + col) * mp + piece) * kD + 4 * grp;
+        float* dst = a.tmp_out + (prow * mp + piece) * kD + 4 * grp;
 #pragma unroll
         for (int db = 0; db < 8; ++db)
           *reinterpret_cast<float4*>(dst + 16 * db) =
               make_float4(st.acc[db][0] * inv, st.acc[db][1] * inv, st.acc[db][2] * inv,
                           st.acc[db][3] * inv);
         if (grp == 0) {
-          a.max_logits[(row0 + col) * mp + piece] = st.m_run * kLn2;  // natural-log units
-          a.exp_sums[(row0 + col) * mp + piece] = l_col;
+          a.max_logits[prow * mp + piece] = st.m_run * kLn2;  // natural-log units
+          a.exp_sums[prow * mp + piece] = l_col;
         }
       }
       if (c.t == c.n - 1 && grp == 0) {
         for (int p = piece + 1; p < mp; ++p) {
-          a.max_logits[(row0 + col) * mp + p] = -INFINITY;
-          a.exp_sums[(row0 + col) * mp + p] = 0.f;
+          a.max_logits[prow * mp + p] = -INFINITY;
+          a.exp_sums[prow * mp + p] = 0.f;
         }
       }
     }
@@ -540,9 +675,9 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     piece = 0;
   };
 
-  // Two register sets, unrolled by two; the q of the next sequence is loaded
-  // before that sequence's first tile, ahead of the tile loads, so a wait for
-  // a tile also covers it. Each processed tile has exactly one tile of loads
+  // Two register sets, unrolled by two; the q of the next unit is loaded
+  // before that unit's first tile, ahead of the tile loads, so a wait for a
+  // tile also covers it. Each processed tile has exactly one tile of loads
   // behind it, or none, on every path.
   TileRegs ta, tb;
   bool ga = geo.load(ta, row_of(cur.s), cur.t * kTile, kvh);
@@ -552,18 +687,20 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   auto step = [&](TileRegs& now, bool g_now, TileRegs& next, bool& g_next) {
     // now = tile i (cur), next <- tile i + 1
     const bool more = i + 1 < len;
-    const bool switch_seq = more && (cur.t + 1 >= cur.n);
+    const bool switch_unit = more && (cur.t + 1 >= cur.n);
+    int slim, vlim;
+    limits(cur, g_now, slim, vlim);
     if (more) {
       nx = advance(cur);
-      if (switch_seq) load_q(qn, a, nx.s, kvh, G, col, grp);
+      if (switch_unit) load_q_unit(qn, nx);
       g_next = geo.load(next, row_of(nx.s), nx.t * kTile, kvh);
       issue_fence();
-      st.tile(now, q, g_now ? cur.ctx - cur.t * kTile : 0, qk_scale, grp, col, slot);
+      st.tile(now, q, slim, vlim, qk_scale, grp, col, slot);
     } else {
-      st.tile(now, q, g_now ? cur.ctx - cur.t * kTile : 0, qk_scale, grp, col, slot);
+      st.tile(now, q, slim, vlim, qk_scale, grp, col, slot);
     }
     if (cur.t + 1 >= cur.n || !more) finish(cur);
-    if (switch_seq) {
+    if (switch_unit) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) q[kk] = qn[kk];
     }
@@ -592,7 +729,7 @@ inline size_t lds_class_bytes(int c) {
   return b[c];
 }
 
-template <typename T>
+template <typename T, bool kVar>
 hipError_t split_grid(int& cus, int& per_cu, size_t dyn) {
   static std::atomic<int> cache[kMaxDevices][kLdsClasses][2];  // 0 = not computed yet
   int dev = 0;
@@ -606,7 +743,7 @@ hipError_t split_grid(int& cus, int& per_cu, size_t dyn) {
   }
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<T>,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<T, kVar>,
                                                      kSplitThreads, lds_class_bytes(c));
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
@@ -617,12 +754,12 @@ hipError_t split_grid(int& cus, int& per_cu, size_t dyn) {
   return hipSuccess;
 }
 
-template <typename T>
+template <typename T, bool kVar>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
-  auto kernel = decode_split_kernel<T>;
+  auto kernel = decode_split_kernel<T, kVar>;
   const size_t dyn = static_cast<size_t>(a.num_seqs + 1) * sizeof(int);
   int cus = 0, per_cu = 0;
-  hipError_t e = split_grid<T>(cus, per_cu, dyn);
+  hipError_t e = split_grid<T, kVar>(cus, per_cu, dyn);
   if (e != hipSuccess) return e;
   const int waves_per_wg = kSplitThreads / 64;
   // whole groups of num_kv_heads waves, no more than the GPU holds at once
@@ -645,7 +782,7 @@ hipError_t launch_whole(const DecodeArgs& a, hipStream_t stream) {
 
 template <typename T>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  return a.partition_size > 0 ? launch_split<T>(a, stream) : launch_whole<T>(a, stream);
+  return a.partition_size > 0 ? launch_split<T, false>(a, stream) : launch_whole<T>(a, stream);
 }
 
 }  // namespace
@@ -662,6 +799,24 @@ bool fast_decode_supported(const DecodeArgs& a) {
 
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream) {
   return a.dtype == 2 ? launch_t<bf16_t>(a, stream) : launch_t<f16_t>(a, stream);
+}
+
+bool fast_varlen_supported(const DecodeArgs& a) {
+  const int G = a.num_heads / a.num_kv_heads;
+  if (!((a.dtype == 1 || a.dtype == 2) && a.head_size == kD && a.block_size % kTile == 0 &&
+        G >= 1 && G <= 16 && a.num_seqs <= kMaxSeqsBalanced))
+    return false;
+  // the stream of (sequence, column group) tiles is indexed with 32 bits: a
+  // sequence has at most q_s / tpg + 1 groups of at most ceil(cap / 16) tiles
+  const int64_t groups = a.num_tokens / (kTile / G) + a.num_seqs;
+  const int64_t cap = static_cast<int64_t>(a.max_blocks) * a.block_size;
+  const int64_t per_group = cap > kTile ? (cap + kTile - 1) / kTile : 1;
+  return groups * per_group <= 0x7fffffff;
+}
+
+hipError_t launch_varlen_fast(const DecodeArgs& a, hipStream_t stream) {
+  return a.dtype == 2 ? launch_split<bf16_t, true>(a, stream)
+                      : launch_split<f16_t, true>(a, stream);
 }
 
 }  // namespace pkv

@@ -17,6 +17,61 @@ namespace {
 
 constexpr int kMaxPerLane = 4;  // head_size <= 256
 
+// Online softmax over positions [lo, hi) of one sequence for one query
+// (q, D values, lane d = lane + 64k), reading KV head kvh. Table entries
+// outside the pool are skipped.
+template <typename T>
+struct Positions {
+  float m = -INFINITY, l = 0.f;
+  float acc[kMaxPerLane] = {0.f, 0.f, 0.f, 0.f};
+
+  __device__ void run(const DecodeArgs& a, const T* __restrict__ q, const int32_t* row,
+                      int kvh, int lo, int hi, int lane) {
+    const int D = a.head_size;
+    const int B = a.block_size;
+    const T* __restrict__ kc = static_cast<const T*>(a.k_cache);
+    const T* __restrict__ vc = static_cast<const T*>(a.v_cache);
+    float qv[kMaxPerLane];
+#pragma unroll
+    for (int k = 0; k < kMaxPerLane; ++k) {
+      const int d = lane + 64 * k;
+      qv[k] = d < D ? to_float(q[d]) : 0.f;
+    }
+    for (int t = lo; t < hi; ++t) {
+      const int64_t blk = physical_block(row, t, B, a.max_blocks, a.num_blocks);
+      if (blk < 0) continue;  // a table entry outside the pool: skipped
+      const int64_t base = pool_row(blk, kvh, t % B, a.num_kv_heads, B, D);
+      float dot = 0.f;
+#pragma unroll
+      for (int k = 0; k < kMaxPerLane; ++k) {
+        const int d = lane + 64 * k;
+        if (d < D) dot = fmaf(qv[k], to_float(kc[base + d]), dot);
+      }
+      const float z = wave_sum(dot) * a.scale;
+      const float m_new = fmaxf(m, z);
+      const float alpha = expf(m - m_new);  // 0 on the first position
+      const float p = expf(z - m_new);
+      l = l * alpha + p;
+#pragma unroll
+      for (int k = 0; k < kMaxPerLane; ++k) {
+        const int d = lane + 64 * k;
+        const float v = d < D ? to_float(vc[base + d]) : 0.f;
+        acc[k] = fmaf(p, v, acc[k] * alpha);
+      }
+      m = m_new;
+    }
+  }
+
+  // normalised output (0 when nothing was attended) into dst[0..D)
+  __device__ void store(float* dst, int D, int lane) const {
+#pragma unroll
+    for (int k = 0; k < kMaxPerLane; ++k) {
+      const int d = lane + 64 * k;
+      if (d < D) dst[d] = l > 0.f ? acc[k] / l : 0.f;
+    }
+  }
+};
+
 template <typename T>
 __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
   const int lane = threadIdx.x;
@@ -26,10 +81,9 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
   const int G = a.num_heads / a.num_kv_heads;
   const int kvh = h / G;
   const int D = a.head_size;
-  const int B = a.block_size;
 
   int ctx = a.context_lens[seq];
-  const int cap = a.max_blocks * B;
+  const int cap = a.max_blocks * a.block_size;
   ctx = ctx < cap ? ctx : cap;
   int lo = 0, hi = ctx;
   if (a.partition_size > 0) {
@@ -46,60 +100,58 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
   }
   const T* __restrict__ q = static_cast<const T*>(a.query) +
                             (static_cast<int64_t>(seq) * a.num_heads + h) * D;
-  const T* __restrict__ kc = static_cast<const T*>(a.k_cache);
-  const T* __restrict__ vc = static_cast<const T*>(a.v_cache);
   const int32_t* __restrict__ row = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
-
-  float qv[kMaxPerLane], acc[kMaxPerLane];
-#pragma unroll
-  for (int k = 0; k < kMaxPerLane; ++k) {
-    const int d = lane + 64 * k;
-    qv[k] = d < D ? to_float(q[d]) : 0.f;
-    acc[k] = 0.f;
-  }
-  float m = -INFINITY, l = 0.f;
-  for (int t = lo; t < hi; ++t) {
-    const int64_t blk = physical_block(row, t, B, a.max_blocks, a.num_blocks);
-    if (blk < 0) continue;  // a table entry outside the pool: skipped
-    const int64_t base = pool_row(blk, kvh, t % B, a.num_kv_heads, B, D);
-    float dot = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMaxPerLane; ++k) {
-      const int d = lane + 64 * k;
-      if (d < D) dot = fmaf(qv[k], to_float(kc[base + d]), dot);
-    }
-    const float z = wave_sum(dot) * a.scale;
-    const float m_new = fmaxf(m, z);
-    const float alpha = expf(m - m_new);  // 0 on the first position
-    const float p = expf(z - m_new);
-    l = l * alpha + p;
-#pragma unroll
-    for (int k = 0; k < kMaxPerLane; ++k) {
-      const int d = lane + 64 * k;
-      const float v = d < D ? to_float(vc[base + d]) : 0.f;
-      acc[k] = fmaf(p, v, acc[k] * alpha);
-    }
-    m = m_new;
-  }
+  Positions<T> st;
+  st.run(a, q, row, kvh, lo, hi, lane);
   const int64_t orow = static_cast<int64_t>(seq) * a.num_heads + h;
   if (a.partition_size > 0) {
     const int64_t pidx = orow * a.max_partitions + part;
-#pragma unroll
-    for (int k = 0; k < kMaxPerLane; ++k) {
-      const int d = lane + 64 * k;
-      if (d < D) a.tmp_out[pidx * D + d] = l > 0.f ? acc[k] / l : 0.f;
-    }
+    st.store(a.tmp_out + pidx * D, D, lane);
     if (lane == 0) {
-      a.max_logits[pidx] = m;
-      a.exp_sums[pidx] = l;
+      a.max_logits[pidx] = st.m;
+      a.exp_sums[pidx] = st.l;
     }
   } else {
-#pragma unroll
-    for (int k = 0; k < kMaxPerLane; ++k) {
-      const int d = lane + 64 * k;
-      if (d < D) a.out[orow * D + d] = l > 0.f ? acc[k] / l : 0.f;
-    }
+    st.store(a.out + orow * D, D, lane);
   }
+}
+
+// Multi-token queries, plain path: one wave per (query row, head). Row r
+// belongs to the sequence s with query_start_loc[s] <= r < query_start_loc[s+1];
+// as token i of that sequence it sits at position ctx - q_s + i and attends
+// positions 0 .. ctx - q_s + i. A row no sequence claims gets 0.
+template <typename T>
+__global__ __launch_bounds__(64) void varlen_generic_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x;
+  const int64_t unit = blockIdx.x;
+  const int r = static_cast<int>(unit / a.num_heads);
+  const int h = static_cast<int>(unit % a.num_heads);
+  const int G = a.num_heads / a.num_kv_heads;
+  const int D = a.head_size;
+  const int32_t* qsl = a.query_start_loc;
+  // largest s with qsl[s] <= r
+  int lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (read_only(qsl + mid) <= r) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo;
+  const int q0 = read_only(qsl + s);
+  const int q1 = read_only(qsl + s + 1);
+  int vis = 0;
+  if (q0 <= r && r < q1) {
+    int ctx = read_only(a.context_lens + s);
+    const int cap = a.max_blocks * a.block_size;
+    ctx = ctx < cap ? ctx : cap;
+    vis = ctx - (q1 - q0) + (r - q0) + 1;
+    vis = vis < 0 ? 0 : (vis > ctx ? ctx : vis);
+  }
+  const T* __restrict__ q = static_cast<const T*>(a.query) +
+                            (static_cast<int64_t>(r) * a.num_heads + h) * D;
+  const int32_t* __restrict__ row = a.block_table + static_cast<int64_t>(s) * a.max_blocks;
+  Positions<T> st;
+  st.run(a, q, row, h / G, 0, vis, lane);
+  st.store(a.out + unit * D, D, lane);
 }
 
 // Merge of split partials: one wave per (sequence, head), four per
@@ -122,7 +174,9 @@ __global__ __launch_bounds__(kRedWaves * 64) void reduce_kernel(
   const int seq = static_cast<int>(unit / num_heads);
   const int D = head_size;
   const int64_t orow = unit;  // = seq * num_heads + h
-  const int n = read_only(context_lens + seq) > 0 ? max_partitions : 0;
+  // without lengths every row takes part (multi-token queries: every query
+  // row's pieces are written, unused ones with l = 0)
+  const int n = (context_lens == nullptr || read_only(context_lens + seq) > 0) ? max_partitions : 0;
   const float* __restrict__ m = max_logits + orow * max_partitions;
   const float* __restrict__ l = exp_sums + orow * max_partitions;
   const float* __restrict__ o = tmp_out + orow * max_partitions * D;
@@ -188,6 +242,16 @@ hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream) {
     case 0: decode_generic_kernel<float><<<grid, block, 0, stream>>>(a); break;
     case 1: decode_generic_kernel<f16_t><<<grid, block, 0, stream>>>(a); break;
     default: decode_generic_kernel<bf16_t><<<grid, block, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_varlen_generic(const DecodeArgs& a, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.num_tokens) * a.num_heads);
+  switch (a.dtype) {
+    case 0: varlen_generic_kernel<float><<<grid, 64, 0, stream>>>(a); break;
+    case 1: varlen_generic_kernel<f16_t><<<grid, 64, 0, stream>>>(a); break;
+    default: varlen_generic_kernel<bf16_t><<<grid, 64, 0, stream>>>(a);
   }
   return hipGetLastError();
 }

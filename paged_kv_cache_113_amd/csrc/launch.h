@@ -40,6 +40,9 @@ struct DecodeArgs {
   float* exp_sums;
   float* tmp_out;
   int dtype;           // pkv_dtype
+  // multi-token queries: [num_seqs + 1] query row starts, NULL for decode
+  const int32_t* query_start_loc;
+  int num_tokens;      // query rows (multi-token queries)
 };
 
 // Matrix-core path: f16/bf16, head_size 128, block_size % 16 == 0, G <= 16.
@@ -48,6 +51,15 @@ hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream);
 // Plain path: every supported shape.
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
 
+// Multi-token queries (query_start_loc set). Matrix-core path: the balanced
+// split kernel over (sequence, column group) units, writing partials for the
+// merge; same shapes as the decode fast path.
+bool fast_varlen_supported(const DecodeArgs& a);
+hipError_t launch_varlen_fast(const DecodeArgs& a, hipStream_t stream);
+// Plain path: one wave per (query row, head), output written directly.
+hipError_t launch_varlen_generic(const DecodeArgs& a, hipStream_t stream);
+
+// context_lens NULL: every row takes part (multi-token queries).
 hipError_t launch_reduce(float* out, const float* max_logits, const float* exp_sums,
                          const float* tmp_out, const int32_t* context_lens, int num_seqs,
                          int num_heads, int head_size, int partition_size, int max_partitions,

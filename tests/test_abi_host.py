@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("paged_kv_write", "paged_decode_attention", "paged_attention_reduce",
               "paged_slot_mapping", "paged_kv_gather", "paged_attention_workspace_bytes",
-              "pkv_strerror"):
+              "paged_varlen_attention", "pkv_strerror"):
         assert n in names
 
 
@@ -88,6 +88,34 @@ def test_attention_validation(lib):
     assert attn(lib, out=None) == ENULL                  # unsplit needs out
     assert attn(lib, psz=32, mp=4) == EWS                # split needs the workspace
     assert attn(lib, psz=32, mp=4, ml=P, es=P) == EWS
+
+
+def varlen(lib, **kw):
+    a = dict(out=P, q=P, k=P, v=P, table=P, qsl=P, ctx=P, S=2, T=9, Hq=8, Hkv=2, D=128, B=16,
+             N=10, MB=4, scale=0.1, mp=8, ml=P, es=P, to=P, dtype=2)
+    a.update(kw)
+    return lib.paged_varlen_attention(a["out"], a["q"], a["k"], a["v"], a["table"], a["qsl"],
+                                      a["ctx"], a["S"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                                      a["B"], a["N"], a["MB"], a["scale"], a["mp"], a["ml"],
+                                      a["es"], a["to"], a["dtype"], None)
+
+
+def test_varlen_validation(lib):
+    assert varlen(lib, dtype=3) == EDTYPE
+    assert varlen(lib, Hq=6, Hkv=4) == ESHAPE
+    assert varlen(lib, T=-1) == ESHAPE
+    assert varlen(lib, S=-2) == ESHAPE
+    assert varlen(lib, mp=0) == ESHAPE
+    assert varlen(lib, N=0) == ESHAPE
+    assert varlen(lib, MB=1 << 28, B=16) == ESHAPE        # positions beyond 32 bits
+    assert varlen(lib, D=300) == EUNSUP
+    assert varlen(lib, T=0) == OK and varlen(lib, S=0) == OK
+    assert varlen(lib, qsl=None) == ENULL
+    assert varlen(lib, out=None) == ENULL
+    assert varlen(lib, ctx=None) == ENULL
+    assert varlen(lib, to=None) == EWS
+    assert varlen(lib, ml=None, dtype=0, D=64) == EWS     # required on every path
+    assert varlen(lib, T=1 << 24, Hq=64, Hkv=8) == EUNSUP  # (row, head) waves beyond 2^26
 
 
 def test_reduce_validation(lib):

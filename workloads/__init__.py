@@ -65,6 +65,8 @@ class Batch:
     sharers: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int32))
     shared_blocks: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int32))
     page_example: bool = False       # tensors come from the glossary page's recipe
+    query_lens: np.ndarray | None = None  # int32 [S]: query tokens per sequence (multi-token
+                                          # queries at the last positions), or None (one each)
 
     @property
     def num_seqs(self) -> int:
@@ -73,6 +75,19 @@ class Batch:
     @property
     def max_blocks(self) -> int:
         return int(self.block_table.shape[1])
+
+    @property
+    def num_tokens(self) -> int:
+        """Query rows: one per sequence, or the sum of query_lens."""
+        if self.query_lens is None:
+            return self.num_seqs
+        return int(self.query_lens.sum())
+
+    @property
+    def query_start_loc(self) -> np.ndarray:
+        """int32 [S + 1]: sequence s owns query rows [qsl[s], qsl[s+1])."""
+        q = np.ones(self.num_seqs, np.int64) if self.query_lens is None else self.query_lens
+        return np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
 
     def live_lens(self) -> np.ndarray:
         """Positions holding data before this step's write (ctx - 1 when a
@@ -221,12 +236,61 @@ def decode_step_bf16(num_seqs: int = 512, lo: int = 64, hi: int = 4096,
                          seed, num_layers=num_layers, new_token=True)
 
 
+def _varlen_case(name, dtype, hq, hkv, d, b, hist, qlens, seed, free_order=None,
+                 rng=None):
+    """Sequences with ``hist`` cached positions and ``qlens`` new query
+    tokens each, whose K/V are already in the pool: ctx = hist + q. Tables
+    dealt from a shuffled free list over ceil(1.1 * need) blocks."""
+    hist = np.asarray(hist, np.int64)
+    qlens = np.asarray(qlens, np.int64)
+    lens = hist + qlens
+    need = int(sum(_nblocks(n, b) for n in lens))
+    n_blocks = max(1, math.ceil(1.1 * need))
+    if free_order is None:
+        rng = np.random.default_rng(seed) if rng is None else rng
+        free_order = rng.permutation(n_blocks).astype(np.int32)
+    table, _ = deal_tables(lens, b, free_order)
+    return Batch(name=name, dtype=dtype, num_heads=hq, num_kv_heads=hkv, head_size=d,
+                 block_size=b, num_blocks=n_blocks, block_table=table,
+                 context_lens=lens.astype(np.int32), free_order=free_order, seed=seed,
+                 query_lens=qlens.astype(np.int32))
+
+
+def spec_verify_bf16(num_seqs: int = 512, draft: int = 4, lo: int = 64, hi: int = 4096,
+                     seed: int = 1006, block_size: int = 16) -> Batch:
+    """Speculative verification in the decode-step geometry (bf16, Hq=32,
+    Hkv=8, D=128, B=16): every sequence brings ``draft`` query tokens on top
+    of U{lo..hi} cached positions."""
+    rng = np.random.default_rng(seed)
+    hist = rng.integers(lo, hi, size=num_seqs, endpoint=True)
+    return _varlen_case("spec_verify_bf16", "bf16", 32, 8, 128, block_size, hist,
+                        np.full(num_seqs, draft), seed, rng=rng)
+
+
+def mixed_prefill_bf16(num_decode: int = 504, num_prefill: int = 8, chunk: int = 512,
+                       lo: int = 64, hi: int = 4096, seed: int = 1007,
+                       block_size: int = 16) -> Batch:
+    """A continuous-batching step in the decode-step geometry (bf16, Hq=32,
+    Hkv=8, D=128, B=16): ``num_decode`` sequences with one new token on
+    U{lo..hi} cached positions, then ``num_prefill`` chunked prefills of
+    ``chunk`` tokens on U{0..hi - chunk} already-computed prompt positions."""
+    rng = np.random.default_rng(seed)
+    hist_d = rng.integers(lo, hi, size=num_decode, endpoint=True)
+    hist_p = rng.integers(0, hi - chunk, size=num_prefill, endpoint=True)
+    hist = np.concatenate([hist_d, hist_p])
+    q = np.concatenate([np.ones(num_decode, np.int64), np.full(num_prefill, chunk)])
+    return _varlen_case("mixed_prefill_bf16", "bf16", 32, 8, 128, block_size, hist, q, seed,
+                        rng=rng)
+
+
 CASES = {
     "tiny": tiny_page_example,
     "mha_fp16": mha_fp16,
     "gqa_shared_bf16": gqa_shared_bf16,
     "long_split_bf16": long_split_bf16,
     "decode_step_bf16": decode_step_bf16,
+    "spec_verify_bf16": spec_verify_bf16,
+    "mixed_prefill_bf16": mixed_prefill_bf16,
 }
 
 
@@ -318,7 +382,7 @@ def layer_tensors(batch: Batch, layer: int = 0, device="cpu", poison: bool = Tru
     n, hkv, b, d = batch.num_blocks, batch.num_kv_heads, batch.block_size, batch.head_size
     rows = max(1, (1 << 26) // (hkv * b * d))  # ~64M elements per draw
     out = {
-        "q": _randn((batch.num_seqs, batch.num_heads, d), base + 0, batch.dtype, device),
+        "q": _randn((batch.num_tokens, batch.num_heads, d), base + 0, batch.dtype, device),
         "k_cache": _randn((n, hkv, b, d), base + 1, batch.dtype, device, rows),
         "v_cache": _randn((n, hkv, b, d), base + 2, batch.dtype, device, rows),
     }
