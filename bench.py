@@ -6,6 +6,11 @@ slot-mapping launch for the batch, then for every layer: the new tokens' K/V
 write, split decode attention (balanced pieces, 1024-position slots) and the
 log-sum-exp merge. Inputs are resident in HBM before timing starts.
 
+Multi-token workloads (``--workload spec_verify_bf16`` / ``mixed_prefill_bf16``):
+one step is one paged_varlen_attention call (balanced split kernel over
+(sequence, column group) units, then the merge over query rows) on one layer,
+with L2/MALL evicted before it.
+
 Prints one JSON line. `value` is KV-read GB/s over the whole step: the
 algorithmic bytes every layer must read (2 * Hkv * D * 2 B per live
 (sequence, position)) divided by the step time. The `roofline` object is for
@@ -71,7 +76,27 @@ def default_partition(workload):
     """Split size per workload: it sizes the partial slots (max_partitions =
     ceil(max ctx / P)); smaller P leaves the balanced split more freedom."""
     return {"decode_step_bf16": 1024, "long_split_bf16": 1024, "mha_fp16": 256,
-            "gqa_shared_bf16": 1024, "tiny": 0}[workload]
+            "gqa_shared_bf16": 1024, "tiny": 0, "spec_verify_bf16": 0,
+            "mixed_prefill_bf16": 0}[workload]
+
+
+VARLEN = ("spec_verify_bf16", "mixed_prefill_bf16")
+
+
+def visible_pairs(batch) -> np.ndarray:
+    """Per query row, how many positions it attends (causal, new tokens at the
+    end of each context): a workload statistic for the flop count."""
+    ctx = batch.context_lens.astype(np.int64)
+    q = batch.query_lens.astype(np.int64)
+    out = []
+    for s in range(batch.num_seqs):
+        out.append(ctx[s] - q[s] + 1 + np.arange(q[s], dtype=np.int64))
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+def visible_pairs_of(batch, s) -> int:
+    c, q = int(batch.context_lens[s]), int(batch.query_lens[s])
+    return q * (c - q) + q * (q + 1) // 2
 
 
 def cpu_baseline(batch, th, target_s: float, threads: int):
@@ -89,11 +114,21 @@ def cpu_baseline(batch, th, target_s: float, threads: int):
         k = oracle.scatter.scatter(k, oracle._raw(th["k_new"], batch.dtype), slots)
         v = oracle.scatter.scatter(v, oracle._raw(th["v_new"], batch.dtype), slots)
     scale = float(np.float32(1.0 / math.sqrt(batch.head_size)))
+    qsl = batch.query_start_loc
 
     def run(seqs, nthreads):
+        if batch.query_lens is None:
+            t0 = time.perf_counter()
+            oracle.attention(th["q"], k, v, batch.block_table, batch.context_lens, scale,
+                             batch.dtype, seqs=seqs, threads=nthreads)
+            return time.perf_counter() - t0
+        rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs])
+        ql = np.array([qsl[s + 1] - qsl[s] for s in seqs], np.int64)
+        sub_qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+        sub_q = th["q"][rows]
         t0 = time.perf_counter()
-        oracle.attention(th["q"], k, v, batch.block_table, batch.context_lens, scale,
-                         batch.dtype, seqs=seqs, threads=nthreads)
+        oracle.attention_varlen(sub_q, k, v, batch.block_table[seqs], sub_qsl,
+                                batch.context_lens[seqs], scale, batch.dtype, threads=nthreads)
         return time.perf_counter() - t0
 
     everything = np.arange(batch.num_seqs, dtype=np.int32)
@@ -103,10 +138,13 @@ def cpu_baseline(batch, th, target_s: float, threads: int):
         reps += 1
     all_rate = kv_bytes(batch, batch.context_lens) * reps / spent
     order = np.random.default_rng(7).permutation(batch.num_seqs).astype(np.int32)
+    # work per sequence: the positions its query rows attend
+    work = batch.context_lens.astype(np.int64) if batch.query_lens is None else np.array(
+        [visible_pairs_of(batch, s) for s in range(batch.num_seqs)], np.int64)
     probe = order[:2]
     dt = run(probe, 1)
-    per_pos = dt / max(1, int(batch.context_lens[probe].sum()))
-    csum = np.cumsum(batch.context_lens[order])
+    per_pos = dt / max(1, int(work[probe].sum()))
+    csum = np.cumsum(work[order])
     n1 = int(max(1, min(len(order), np.searchsorted(csum, (target_s / 2) / per_pos) + 1)))
     dt1 = run(order[:n1], 1)
     one_rate = kv_bytes(batch, batch.context_lens[order[:n1]]) / dt1
@@ -128,7 +166,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode_step_bf16",
                     choices=["decode_step_bf16", "mha_fp16", "gqa_shared_bf16",
-                             "long_split_bf16"])
+                             "long_split_bf16", *VARLEN])
+    ap.add_argument("--max-partitions", type=int, default=8,
+                    help="multi-token workloads: pieces per query row at most")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="decode step only (default 32)")
     ap.add_argument("--block-size", type=int, default=None,
@@ -159,6 +199,9 @@ def main():
     L = batch.num_layers
     P = default_partition(args.workload) if args.partition_size is None else args.partition_size
     mp = batch.max_partitions(P) if P > 0 else 1
+    varlen = args.workload in VARLEN
+    if varlen:
+        mp = args.max_partitions
     scale = float(np.float32(1.0 / math.sqrt(batch.head_size)))
     print(f"[bench] workload {args.workload}: S={batch.num_seqs} layers={L} "
           f"blocks/layer={batch.num_blocks} P={P}", file=sys.stderr, flush=True)
@@ -179,10 +222,11 @@ def main():
     ctx = torch.as_tensor(batch.context_lens, device=dev)
     pos = torch.as_tensor(batch.positions, device=dev) if batch.positions is not None else None
     slots = torch.empty(batch.num_seqs, dtype=torch.int64, device=dev)
-    outs = [torch.empty(batch.num_seqs, batch.num_heads, batch.head_size, device=dev)
+    outs = [torch.empty(batch.num_tokens, batch.num_heads, batch.head_size, device=dev)
             for _ in range(L)]
-    if P > 0:
-        ws_shape = (batch.num_seqs, batch.num_heads, mp)
+    qsl = torch.as_tensor(batch.query_start_loc, device=dev)
+    if P > 0 or varlen:
+        ws_shape = (batch.num_tokens, batch.num_heads, mp)
         ml = torch.empty(ws_shape, device=dev)
         es = torch.empty(ws_shape, device=dev)
         to = torch.empty(ws_shape + (batch.head_size,), device=dev)
@@ -214,7 +258,11 @@ def main():
             if pos is not None:
                 timed("write", record, lambda: pkv.paged_kv_write(
                     t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], slots))
-            if P > 0:
+            if varlen:
+                timed("decode", record, lambda: pkv.paged_varlen_attention(
+                    outs[l], t["q"], t["k_cache"], t["v_cache"], table, qsl, ctx, scale, mp, ml,
+                    es, to))
+            elif P > 0:
                 timed("decode", record, lambda: pkv.paged_decode_attention(
                     None, t["q"], t["k_cache"], t["v_cache"], table, ctx, scale, P, mp, ml, es,
                     to))
@@ -286,6 +334,8 @@ def main():
     achieved = layer_bytes / (dec_ms / 1e3) / 1e9
     positions = float(np.sum(batch.context_lens, dtype=np.int64))
     traffic = traffic_for(args.workload, layer_bytes)
+    pairs = float(visible_pairs(batch).sum()) if varlen else positions
+    flops = 4.0 * batch.num_heads * batch.head_size * pairs   # q.K and P.V, per layer
 
     cpu = None
     if cpu_host is not None:
@@ -300,6 +350,10 @@ def main():
               "context_lens": f"{int(batch.context_lens.min())}..{int(batch.context_lens.max())}"
                               f" mean {float(batch.context_lens.mean()):.1f}",
               "partition_size": P, "blocks_per_layer": batch.num_blocks}
+    if varlen:
+        config.update({"num_tokens": batch.num_tokens, "max_partitions": mp,
+                       "query_lens": f"{int(batch.query_lens.min())}..{int(batch.query_lens.max())}"
+                                     f" total {batch.num_tokens}"})
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -307,6 +361,9 @@ def main():
         "dtype": batch.dtype, "data": "synthetic", "config": config,
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_tokens_per_s": round(positions * L / (ms_per_step / 1e3), 1),
+        "query_pairs_per_s": round(pairs * L / (ms_per_step / 1e3), 1) if varlen else None,
+        "query_tokens_per_s": round(batch.num_tokens * L / (ms_per_step / 1e3), 1)
+        if varlen else None,
         "new_tokens_per_s": round(batch.num_seqs / (ms_per_step / 1e3), 1)
         if batch.positions is not None else None,
         "kernels_ms": {"decode_avg": round(dec_ms, 4), "decode_p10": round(dec_p10, 4),
@@ -314,9 +371,15 @@ def main():
                        "write_avg": round(wr_ms, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_split_kernel" if P > 0
-                     else "decode_whole_kernel", "bytes_per_launch": layer_bytes,
-                     "logical_bytes_per_launch": logical_bytes},
+                     "traffic": traffic,
+                     "kernel": "paged_varlen_attention (split kernel + merge)" if varlen
+                     else "decode_split_kernel" if P > 0 else "decode_whole_kernel",
+                     "bytes_per_launch": layer_bytes,
+                     "logical_bytes_per_launch": logical_bytes,
+                     "mfma_view": {"flops_per_launch": flops,
+                                   "achieved_tflops": round(flops / (dec_ms / 1e3) / 1e12, 2),
+                                   "peak_tflops": 2500.0,
+                                   "frac": round(flops / (dec_ms / 1e3) / 2.5e15, 4)}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
