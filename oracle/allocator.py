@@ -20,6 +20,15 @@ Sources (page titles as printed at the head of each page):
     allocated slots and the slots saved by sharing a prefix block.
   * nxmr.cn article, section 5.2: block utilisation = live tokens /
     (allocated blocks * B).
+  * nxmr.cn article, sections 4.1-4.3 (copy-on-write): branches of one
+    sequence (beam search, parallel sampling) share its blocks by reference;
+    a full block is immutable and safely shared; before a sequence writes
+    into its last, partly filled block it checks the block's reference
+    count: 1 -> write in place; > 1 -> take a fresh block, copy the old
+    block's contents into it, point the table entry at it, drop one
+    reference from the old block, then write. A full last block means a
+    fresh block and no copy. The paper-notes page adds that only the one
+    modified block is copied, never the whole cache, as with Unix fork().
 
 The free list is a plain deque; the pages' O(1) intrusive list is only needed
 for prefix-cache eviction, which this oracle does not model.
@@ -128,6 +137,43 @@ class BlockAllocator:
         self.tables[rid].extend(got)
         self.lengths[rid] = old + new_tokens
         return got
+
+    def fork(self, parent, child) -> list:
+        """``child`` starts as a copy of ``parent``: the same blocks, by
+        reference (every block gains one reference), the same length."""
+        if child in self.tables:
+            raise KeyError(child)
+        blocks = list(self.tables[parent])
+        for b in blocks:
+            self._acquire(b)
+        self.tables[child] = blocks
+        self.lengths[child] = self.lengths[parent]
+        return list(blocks)
+
+    def append_slot(self, rid):
+        """Make room for one more token of ``rid`` (copy-on-write rule).
+
+        Returns (slot, copy): the slot the new token goes to, and (src, dst)
+        when the last block had to be copied first, else None. Atomic: on
+        MemoryError nothing changes.
+        """
+        n = self.lengths[rid]
+        table = self.tables[rid]
+        used = n % self.block_size
+        if used == 0:                      # no block, or the last one is full
+            (fresh,) = self._take(1)
+            table.append(fresh)
+            self.lengths[rid] = n + 1
+            return fresh * self.block_size, None
+        last = table[-1]
+        if self.ref[last] == 1:            # sole owner: write in place
+            self.lengths[rid] = n + 1
+            return last * self.block_size + used, None
+        (fresh,) = self._take(1)           # shared partial block: copy on write
+        table[-1] = fresh
+        self._release(last)
+        self.lengths[rid] = n + 1
+        return fresh * self.block_size + used, (last, fresh)
 
     def free_request(self, rid) -> None:
         """Release every block of ``rid`` in table order."""

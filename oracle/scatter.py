@@ -1,4 +1,5 @@
-"""New-token K/V write into the paged pool: the oracle's plain definition.
+"""New-token K/V write and whole-block copy in the paged pool: the oracle's
+plain definitions.
 
 TEST INFRASTRUCTURE ONLY (tests/, smoke check, CPU baseline leg of bench.py).
 
@@ -7,6 +8,10 @@ Source: "vLLM PagedAttention: from fragmentation to slot mapping", section 6
 and section 3 (one slot holds one token's [num_kv_heads, head_dim] K and V
 for a layer). Slot s lives in block s // B at offset s % B of a
 [num_blocks, Hkv, B, D] pool. A negative slot means "no write".
+
+Block copy (copy-on-write, nxmr.cn article, section 4.2: the old block's
+KV data is copied into the fresh block): every byte of block dst, all KV
+heads and all slots, becomes the byte of block src.
 
 Works on raw bytes (numpy views of any element type), so the comparison with
 the GPU is bitwise.
@@ -31,4 +36,22 @@ def scatter(pool: np.ndarray, new: np.ndarray, slots) -> np.ndarray:
         assert s not in seen, f"slot {s} written twice"
         seen.add(s)
         out[s // block_size, :, s % block_size, :] = new[i]
+    return out
+
+
+def copy_blocks(pool: np.ndarray, pairs) -> np.ndarray:
+    """Return a copy of ``pool`` [N, Hkv, B, D] in which block dst holds the
+    old contents of block src for every (src, dst) in ``pairs``. Destinations
+    are distinct and no destination is another pair's source, so the result
+    does not depend on the order of the pairs."""
+    out = pool.copy()
+    n_blocks = pool.shape[0]
+    dsts = [int(d) for _, d in pairs]
+    srcs = {int(s) for s, _ in pairs}
+    assert len(set(dsts)) == len(dsts), "a block is copied into twice"
+    assert not srcs & set(dsts), "a destination is also a source"
+    for s, d in pairs:
+        s, d = int(s), int(d)
+        assert 0 <= s < n_blocks and 0 <= d < n_blocks
+        out[d] = pool[s]
     return out

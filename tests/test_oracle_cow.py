@@ -1,0 +1,207 @@
+"""Pins for the oracle's copy-on-write: fork, the append rule and the block
+copy.
+
+  * tests/golden/cow.json: the nxmr.cn article's section 4.2 rule applied by
+    hand to a FIFO pool (every case of the rule: write in place, copy a
+    shared partial block, fresh block after a full one with no copy, freeing
+    a branch);
+  * a token-level simulation over random add / fork / append / free
+    sequences: after every step each live sequence reads back exactly its
+    own token history through its table (no branch ever overwrote another's
+    data), reference counts equal the number of tables holding each block,
+    the free list holds exactly the unreferenced blocks, a full block is
+    never written or copied, and each append copies at most one block (the
+    paper-notes page: only the modified block);
+  * planted mistakes in the rule fail the simulation;
+  * the block copy against a per-element loop.
+"""
+import numpy as np
+import pytest
+
+from oracle import allocator as A
+from oracle.scatter import copy_blocks
+
+
+def test_cow_timeline(golden):
+    g = golden("cow.json")
+    a = A.BlockAllocator(g["num_blocks"], g["block_size"])
+    for st in g["steps"]:
+        if st["op"] == "add":
+            a.add(st["rid"], st["n"])
+        elif st["op"] == "fork":
+            a.fork(st["rid"], st["child"])
+        elif st["op"] == "append":
+            slot, cp = a.append_slot(st["rid"])
+            assert slot == st["slot"], st
+            assert (list(cp) if cp else None) == st["copy"], st
+        else:
+            a.free_request(st["rid"])
+        assert a.tables == st["tables"], st
+        assert a.free_list() == st["free"], st
+    assert a.ref == g["final_refs"]
+    assert a.lengths == g["final_lengths"]
+
+
+def test_append_is_atomic_when_the_pool_is_empty():
+    a = A.BlockAllocator(2, 4)
+    a.add("p", 3)
+    a.fork("p", "q")
+    a.add("r", 1)                      # takes the last free block
+    before = (a.free_list(), {k: v[:] for k, v in a.tables.items()}, dict(a.lengths),
+              list(a.ref))
+    with pytest.raises(MemoryError):
+        a.append_slot("q")             # would need a fresh block for the copy
+    assert before == (a.free_list(), {k: v[:] for k, v in a.tables.items()},
+                      dict(a.lengths), list(a.ref))
+    with pytest.raises(KeyError):
+        a.fork("p", "q")
+
+
+class _Sim:
+    """Slot contents as token ids; copies and writes applied as the
+    allocator dictates."""
+
+    def __init__(self, alloc):
+        self.a = alloc
+        self.B = alloc.block_size
+        self.slots = {}
+        self.hist = {}
+        self.next_tok = 1
+        self.writes_to_full = 0
+
+    def _write(self, slot, tok):
+        self.slots[slot] = tok
+
+    def add(self, rid, n):
+        self.a.add(rid, n)
+        toks = list(range(self.next_tok, self.next_tok + n))
+        self.next_tok += n
+        for p, t in enumerate(toks):
+            self._write(self.a.slot(rid, p), t)
+        self.hist[rid] = toks
+
+    def fork(self, parent, child):
+        self.a.fork(parent, child)
+        self.hist[child] = list(self.hist[parent])
+
+    def append(self, rid):
+        slot, cp = self.a.append_slot(rid)
+        copies = 0
+        if cp is not None:
+            src, dst = cp
+            # only a partly filled last block is copied: the new token does
+            # not start the fresh block
+            assert slot // self.B == dst and slot % self.B != 0
+            for o in range(self.B):
+                if src * self.B + o in self.slots:
+                    self.slots[dst * self.B + o] = self.slots[src * self.B + o]
+            copies = 1
+        tok = self.next_tok
+        self.next_tok += 1
+        blk = slot // self.B
+        # the block written to is referenced by this sequence alone
+        assert self.a.ref[blk] == 1, "write into a shared block"
+        self._write(slot, tok)
+        self.hist[rid].append(tok)
+        return copies
+
+    def free(self, rid):
+        self.a.free_request(rid)
+        del self.hist[rid]
+
+    def check(self):
+        a = self.a
+        for rid, h in self.hist.items():
+            assert a.lengths[rid] == len(h)
+            got = [self.slots.get(a.slot(rid, p)) for p in range(len(h))]
+            assert got == h, f"sequence {rid} reads {got}, wrote {h}"
+        held = [0] * a.num_blocks
+        for t in a.tables.values():
+            for b in t:
+                held[b] += 1
+        assert held == a.ref
+        assert sorted(a.free_list()) == [b for b in range(a.num_blocks) if a.ref[b] == 0]
+        assert len(set(a.free_list())) == len(a.free_list())
+
+
+def _random_run(seed, alloc_cls=A.BlockAllocator):
+    rng = np.random.default_rng(seed)
+    B = int(rng.choice([1, 2, 4, 8]))
+    sim = _Sim(alloc_cls(64, B, rng.permutation(64).tolist()))
+    names = 0
+    for _ in range(200):
+        live = list(sim.hist)
+        op = rng.choice(["add", "fork", "append", "append", "append", "free"])
+        try:
+            if op == "add" or not live:
+                sim.add(f"r{names}", int(rng.integers(1, 3 * B + 2)))
+                names += 1
+            elif op == "fork":
+                sim.fork(live[int(rng.integers(len(live)))], f"r{names}")
+                names += 1
+            elif op == "append":
+                assert sim.append(live[int(rng.integers(len(live)))]) <= 1
+            else:
+                sim.free(live[int(rng.integers(len(live)))])
+        except MemoryError:
+            pass
+        sim.check()
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_cow_simulation_keeps_every_branch_intact(seed):
+    _random_run(seed)
+
+
+class _InPlaceWhenShared(A.BlockAllocator):
+    def append_slot(self, rid):
+        n = self.lengths[rid]
+        if n % self.block_size:
+            self.lengths[rid] = n + 1
+            return self.tables[rid][-1] * self.block_size + n % self.block_size, None
+        return super().append_slot(rid)
+
+
+class _CopyWithoutRelease(A.BlockAllocator):
+    def _release(self, block):
+        import inspect
+        if inspect.stack()[1].function == "append_slot":
+            return
+        super()._release(block)
+
+
+class _NoCopy(A.BlockAllocator):
+    def append_slot(self, rid):
+        slot, cp = super().append_slot(rid)
+        return slot, None
+
+
+@pytest.mark.parametrize("cls", [_InPlaceWhenShared, _CopyWithoutRelease, _NoCopy])
+def test_planted_cow_mistakes_fail_the_simulation(cls):
+    failures = 0
+    for seed in range(10):
+        try:
+            _random_run(seed, cls)
+        except AssertionError:
+            failures += 1
+    assert failures >= 5
+
+
+def test_copy_blocks_definition():
+    rng = np.random.default_rng(2)
+    pool = rng.integers(0, 1 << 16, size=(9, 3, 4, 5), dtype=np.uint16)
+    pairs = [(1, 7), (1, 8), (4, 2)]
+    got = copy_blocks(pool, pairs)
+    want = pool.copy()
+    for s, d in pairs:
+        for h in range(3):
+            for o in range(4):
+                for e in range(5):
+                    want[d, h, o, e] = pool[s, h, o, e]
+    assert np.array_equal(got, want)
+    assert np.array_equal(copy_blocks(pool, pairs[::-1]), got)   # order does not matter
+    assert np.array_equal(copy_blocks(pool, []), pool)
+    with pytest.raises(AssertionError):
+        copy_blocks(pool, [(1, 7), (2, 7)])
+    with pytest.raises(AssertionError):
+        copy_blocks(pool, [(1, 7), (7, 3)])
