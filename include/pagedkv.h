@@ -62,7 +62,8 @@ enum pkv_status {
   PKV_ERR_DTYPE = -3,       /* unknown dtype code */
   PKV_ERR_UNSUPPORTED = -4, /* valid, but no kernel handles this shape */
   PKV_ERR_WORKSPACE = -5,   /* split requested without its workspace */
-  PKV_ERR_LAUNCH = -6       /* the HIP runtime refused a launch */
+  PKV_ERR_LAUNCH = -6,      /* the HIP runtime refused a launch */
+  PKV_ERR_HOST = -7         /* a host buffer is too small or not pinned memory */
 };
 
 /*
@@ -245,6 +246,75 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v
                     const int32_t* block_table, const int32_t* context_lens, int num_seqs,
                     int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
                     int max_blocks_per_seq, int max_ctx, int dtype, void* stream);
+
+/*
+ * paged_kv_copy_blocks -- copy whole blocks inside every layer's pools
+ * (copy-on-write).
+ *
+ * Branches of a sequence (beam search, parallel sampling) share its blocks
+ * by reference. A full block never changes and stays shared; before a branch
+ * writes into its last, partly filled block while other branches still
+ * reference it, the host allocator gives it a fresh block, and this call
+ * copies the old block's KV data there (nxmr.cn article, sections 4.2-4.3;
+ * only the modified block is copied, never the whole cache: paper-notes
+ * page, beam search and parallel sampling). For every layer l < num_layers
+ * and every pair i with src = block_mapping[2i], dst = block_mapping[2i+1]:
+ *   k_caches[l][dst] = k_caches[l][src], v_caches[l][dst] = v_caches[l][src]
+ * (all num_kv_heads x block_size x head_size elements, a bit copy).
+ *
+ * k_caches, v_caches: HOST arrays of num_layers device pointers, each a
+ * [num_blocks, num_kv_heads, block_size, head_size] pool of `dtype`.
+ * block_mapping: DEVICE int64 [num_pairs, 2]. A pair with an id outside
+ * [0, num_blocks), or src == dst, is skipped. Preconditions: destinations
+ * are distinct and none is another pair's source (then the order of the
+ * pairs does not matter).
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_UNSUPPORTED
+ * (2^24 pairs or more), PKV_ERR_LAUNCH. num_layers == 0 or num_pairs == 0
+ * is a no-op.
+ */
+int paged_kv_copy_blocks(void* const* k_caches, void* const* v_caches, int num_layers,
+                         const int64_t* block_mapping, int64_t num_pairs, int64_t num_blocks,
+                         int num_kv_heads, int block_size, int head_size, int dtype,
+                         void* stream);
+
+/*
+ * paged_kv_swap_out / paged_kv_swap_in -- move whole blocks between every
+ * layer's pools and pinned host memory (preemption by swapping).
+ *
+ * A preempted request's KV blocks are copied from GPU to CPU memory and
+ * back when the GPU has room again (paper-notes page, preemption: swapping
+ * vs recomputation); on the way back they go to newly allocated blocks and
+ * the request's table is rewritten to them (nxmr.cn article, section 6.2).
+ * With slab = num_kv_heads * block_size * head_size elements:
+ *   swap_out: host[l][0][i] = k_caches[l][block_ids[i]],
+ *             host[l][1][i] = v_caches[l][block_ids[i]];
+ *   swap_in:  k_caches[l][block_ids[i]] = host[l][0][i], likewise V,
+ * for l < num_layers, i < num_ids (a bit copy). The host buffer is
+ * [num_layers, 2, num_ids, slab] in `dtype` and host_bytes is its size.
+ *
+ * host buffer: pinned host memory (hipHostMalloc, or a torch tensor made
+ * with pin_memory=True), read or written by the kernels directly over the
+ * host link; the library queries the pointer and refuses anything else with
+ * PKV_ERR_HOST (also when host_bytes is short) before launching. Like every
+ * call here it only enqueues: the host data is complete (swap_out) or may be
+ * reused (swap_in) once the stream has reached the call.
+ * k_caches, v_caches: HOST arrays of num_layers device pool pointers.
+ * block_ids: DEVICE int64 [num_ids]; an id outside [0, num_blocks) is
+ * skipped (its host slab is untouched). swap_in destinations must be
+ * distinct.
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_HOST,
+ * PKV_ERR_UNSUPPORTED (2^24 ids or more), PKV_ERR_LAUNCH. num_layers == 0 or
+ * num_ids == 0 is a no-op. These two calls make one HIP query (the pointer
+ * check) before they launch; every other argument check precedes it.
+ */
+int paged_kv_swap_out(void* host_dst, int64_t host_bytes, void* const* k_caches,
+                      void* const* v_caches, int num_layers, const int64_t* block_ids,
+                      int64_t num_ids, int64_t num_blocks, int num_kv_heads, int block_size,
+                      int head_size, int dtype, void* stream);
+int paged_kv_swap_in(const void* host_src, int64_t host_bytes, void* const* k_caches,
+                     void* const* v_caches, int num_layers, const int64_t* block_ids,
+                     int64_t num_ids, int64_t num_blocks, int num_kv_heads, int block_size,
+                     int head_size, int dtype, void* stream);
 
 /* pkv_strerror -- static description of a pkv_status code. */
 const char* pkv_strerror(int code);

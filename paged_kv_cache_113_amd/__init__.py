@@ -30,6 +30,12 @@ SIGNATURES = {
     "paged_varlen_attention": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                       _I32, _I32, _I64, _I32, _F32, _I32, _P, _P, _P, _I32,
                                       _P]),
+    "paged_kv_copy_blocks": (_I32, [_P, _P, _I32, _P, _I64, _I64, _I32, _I32, _I32, _I32,
+                                    _P]),
+    "paged_kv_swap_out": (_I32, [_P, _I64, _P, _P, _I32, _P, _I64, _I64, _I32, _I32, _I32,
+                                 _I32, _P]),
+    "paged_kv_swap_in": (_I32, [_P, _I64, _P, _P, _I32, _P, _I64, _I64, _I32, _I32, _I32,
+                                _I32, _P]),
     "paged_attention_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "paged_kv_gather": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32,
                                _I32, _I32, _P]),
@@ -145,6 +151,61 @@ def paged_varlen_attention(out, query, k_cache, v_cache, block_table, query_star
         _ptr(query_start_loc), _ptr(context_lens), context_lens.shape[0], t, hq, hkv, d, b, n,
         block_table.shape[1], float(scale), max_partitions, _ptr(max_logits), _ptr(exp_sums),
         _ptr(tmp_out), _DTYPE[query.dtype], _stream(stream)))
+
+
+def _pool_ptrs(k_caches, v_caches):
+    """Host arrays of the layers' pool pointers, and the shared geometry."""
+    if len(k_caches) != len(v_caches) or not k_caches:
+        raise ValueError("one K and one V pool per layer")
+    _dev(*k_caches, *v_caches)
+    shape, dtype = k_caches[0].shape, k_caches[0].dtype
+    for t in (*k_caches, *v_caches):
+        if t.shape != shape or t.dtype != dtype:
+            raise ValueError("every layer's pools share one shape and dtype")
+    arr = (ctypes.c_void_p * len(k_caches))
+    kp = arr(*[t.data_ptr() for t in k_caches])
+    vp = arr(*[t.data_ptr() for t in v_caches])
+    return kp, vp, shape, dtype
+
+
+def paged_kv_copy_blocks(k_caches, v_caches, block_mapping, stream=None):
+    """Copy block src -> dst in every layer's K and V pool, for each row
+    (src, dst) of block_mapping [n, 2] int64 (copy-on-write)."""
+    kp, vp, (n, hkv, b, d), dtype = _pool_ptrs(k_caches, v_caches)
+    _dev(block_mapping)
+    assert block_mapping.dtype == torch.int64 and block_mapping.shape[-1] == 2
+    _check("paged_kv_copy_blocks", lib.paged_kv_copy_blocks(
+        kp, vp, len(k_caches), _ptr(block_mapping), block_mapping.shape[0], n, hkv, b, d,
+        _DTYPE[dtype], _stream(stream)))
+
+
+def _host_buf(host, n_layers, n_ids, shape, dtype):
+    if host.is_cuda or not host.is_contiguous() or host.dtype != dtype:
+        raise ValueError("the host buffer is a contiguous CPU tensor of the pools' dtype")
+    return ctypes.c_void_p(host.data_ptr()), host.numel() * host.element_size()
+
+
+def paged_kv_swap_out(host_dst, k_caches, v_caches, block_ids, stream=None):
+    """host_dst [L, 2, n, Hkv, B, D] (pinned) <- blocks block_ids of every
+    layer's K (index 0) and V (index 1) pool."""
+    kp, vp, (n, hkv, b, d), dtype = _pool_ptrs(k_caches, v_caches)
+    _dev(block_ids)
+    assert block_ids.dtype == torch.int64
+    hp, nbytes = _host_buf(host_dst, len(k_caches), block_ids.numel(), (hkv, b, d), dtype)
+    _check("paged_kv_swap_out", lib.paged_kv_swap_out(
+        hp, nbytes, kp, vp, len(k_caches), _ptr(block_ids), block_ids.numel(), n, hkv, b, d,
+        _DTYPE[dtype], _stream(stream)))
+
+
+def paged_kv_swap_in(host_src, k_caches, v_caches, block_ids, stream=None):
+    """Blocks block_ids of every layer's pools <- host_src [L, 2, n, Hkv, B, D]."""
+    kp, vp, (n, hkv, b, d), dtype = _pool_ptrs(k_caches, v_caches)
+    _dev(block_ids)
+    assert block_ids.dtype == torch.int64
+    hp, nbytes = _host_buf(host_src, len(k_caches), block_ids.numel(), (hkv, b, d), dtype)
+    _check("paged_kv_swap_in", lib.paged_kv_swap_in(
+        hp, nbytes, kp, vp, len(k_caches), _ptr(block_ids), block_ids.numel(), n, hkv, b, d,
+        _DTYPE[dtype], _stream(stream)))
 
 
 def paged_attention_workspace_bytes(num_seqs, num_heads, head_size, max_partitions):

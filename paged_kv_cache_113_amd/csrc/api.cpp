@@ -23,6 +23,56 @@ int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUN
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Checks shared by the whole-block moves; 0 when the geometry is valid.
+int move_checks(void* const* k_caches, void* const* v_caches, int num_layers, int64_t n,
+                int64_t num_blocks, int num_kv_heads, int block_size, int head_size,
+                int dtype, int64_t* slab_bytes) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return PKV_ERR_DTYPE;
+  if (num_layers < 0 || n < 0 || num_blocks < 1 || num_kv_heads < 1 || block_size < 1 ||
+      head_size < 1)
+    return PKV_ERR_SHAPE;
+  if (num_layers == 0 || n == 0) return PKV_OK;
+  if (!k_caches || !v_caches) return PKV_ERR_NULL;
+  for (int l = 0; l < num_layers; ++l)
+    if (!k_caches[l] || !v_caches[l]) return PKV_ERR_NULL;
+  // one 256-lane workgroup per slab: the grid's x extent in lanes stays
+  // below 2^32
+  if (n >= (int64_t{1} << 24)) return PKV_ERR_UNSUPPORTED;
+  *slab_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_size * eb;
+  return PKV_OK;
+}
+
+// The device-visible address of a pinned host buffer, or nullptr. Pinned
+// host memory on this platform is reached at its host address; anything
+// else (pageable memory, device memory, another mapping) is refused.
+void* pinned_device_address(const void* host) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, host) != hipSuccess) {
+    (void)hipGetLastError();  // a failed query must not surface as a launch error
+    return nullptr;
+  }
+  if (attr.type != hipMemoryTypeHost) return nullptr;
+  if (attr.devicePointer != host && attr.devicePointer != attr.hostPointer) return nullptr;
+  return const_cast<void*>(host);
+}
+
+int swap_common(void* host, int64_t host_bytes, void* const* k_caches, void* const* v_caches,
+                int num_layers, const int64_t* block_ids, int64_t num_ids, int64_t num_blocks,
+                int num_kv_heads, int block_size, int head_size, int dtype, bool out,
+                void* stream) {
+  int64_t slab = 0;
+  const int rc = move_checks(k_caches, v_caches, num_layers, num_ids, num_blocks, num_kv_heads,
+                             block_size, head_size, dtype, &slab);
+  if (rc != PKV_OK || num_layers == 0 || num_ids == 0) return rc;
+  if (!host || !block_ids) return PKV_ERR_NULL;
+  if (host_bytes / slab / 2 / num_layers < num_ids) return PKV_ERR_HOST;  // too small
+  void* dev = pinned_device_address(host);
+  if (!dev) return PKV_ERR_HOST;
+  pkv::MoveArgs m{k_caches, v_caches, num_layers, dev, block_ids, num_ids, num_blocks, slab};
+  return launch_status(pkv::launch_swap(m, out, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -175,6 +225,37 @@ int paged_varlen_attention(float* out, const void* query, const void* k_cache,
                                           as_stream(stream)));
 }
 
+int paged_kv_copy_blocks(void* const* k_caches, void* const* v_caches, int num_layers,
+                         const int64_t* block_mapping, int64_t num_pairs, int64_t num_blocks,
+                         int num_kv_heads, int block_size, int head_size, int dtype,
+                         void* stream) {
+  int64_t slab = 0;
+  const int rc = move_checks(k_caches, v_caches, num_layers, num_pairs, num_blocks,
+                             num_kv_heads, block_size, head_size, dtype, &slab);
+  if (rc != PKV_OK || num_layers == 0 || num_pairs == 0) return rc;
+  if (!block_mapping) return PKV_ERR_NULL;
+  pkv::MoveArgs m{k_caches, v_caches, num_layers, nullptr, block_mapping, num_pairs,
+                  num_blocks, slab};
+  return launch_status(pkv::launch_copy_blocks(m, as_stream(stream)));
+}
+
+int paged_kv_swap_out(void* host_dst, int64_t host_bytes, void* const* k_caches,
+                      void* const* v_caches, int num_layers, const int64_t* block_ids,
+                      int64_t num_ids, int64_t num_blocks, int num_kv_heads, int block_size,
+                      int head_size, int dtype, void* stream) {
+  return swap_common(host_dst, host_bytes, k_caches, v_caches, num_layers, block_ids, num_ids,
+                     num_blocks, num_kv_heads, block_size, head_size, dtype, true, stream);
+}
+
+int paged_kv_swap_in(const void* host_src, int64_t host_bytes, void* const* k_caches,
+                     void* const* v_caches, int num_layers, const int64_t* block_ids,
+                     int64_t num_ids, int64_t num_blocks, int num_kv_heads, int block_size,
+                     int head_size, int dtype, void* stream) {
+  return swap_common(const_cast<void*>(host_src), host_bytes, k_caches, v_caches, num_layers,
+                     block_ids, num_ids, num_blocks, num_kv_heads, block_size, head_size, dtype,
+                     false, stream);
+}
+
 size_t paged_attention_workspace_bytes(int num_seqs, int num_heads, int head_size,
                                        int max_partitions) {
   if (num_seqs <= 0 || num_heads <= 0 || head_size <= 0 || max_partitions <= 0) return 0;
@@ -212,6 +293,7 @@ const char* pkv_strerror(int code) {
     case PKV_ERR_UNSUPPORTED: return "no kernel handles this shape";
     case PKV_ERR_WORKSPACE: return "split mode needs max_logits, exp_sums and tmp_out";
     case PKV_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    case PKV_ERR_HOST: return "the host buffer is too small or not pinned memory the GPU reaches";
     default: return "unknown pkv status code";
   }
 }

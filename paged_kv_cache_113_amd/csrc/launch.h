@@ -65,4 +65,25 @@ hipError_t launch_reduce(float* out, const float* max_logits, const float* exp_s
                          int num_heads, int head_size, int partition_size, int max_partitions,
                          hipStream_t stream);
 
+// Whole-block moves (copy-on-write copies, swap out / in), one workgroup per
+// (slab, layer, K or V); up to kMaxLayersPerLaunch layers' pool pointers ride
+// in the kernel arguments, more layers take more launches.
+constexpr int kMaxLayersPerLaunch = 64;
+struct LayerPtrs {
+  char* k[kMaxLayersPerLaunch];
+  char* v[kMaxLayersPerLaunch];
+};
+struct MoveArgs {
+  void* const* k_caches;  // host array [num_layers] of device pool pointers
+  void* const* v_caches;
+  int num_layers;
+  void* host;             // swap: device-visible address of the pinned buffer
+  const int64_t* ids;     // device: (src, dst) pairs [n][2] (copy) or block ids [n]
+  int64_t n;
+  int64_t num_blocks;
+  int64_t slab_bytes;     // Hkv * B * D * element bytes
+};
+hipError_t launch_copy_blocks(const MoveArgs& m, hipStream_t stream);
+hipError_t launch_swap(const MoveArgs& m, bool out, hipStream_t stream);
+
 }  // namespace pkv

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("paged_kv_write", "paged_decode_attention", "paged_attention_reduce",
               "paged_slot_mapping", "paged_kv_gather", "paged_attention_workspace_bytes",
-              "paged_varlen_attention", "pkv_strerror"):
+              "paged_varlen_attention", "paged_kv_copy_blocks", "paged_kv_swap_out",
+              "paged_kv_swap_in", "pkv_strerror"):
         assert n in names
 
 
@@ -45,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_strerror(lib):
-    for code in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, ELAUNCH):
+    for code in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, ELAUNCH, -7):
         assert len(lib.pkv_strerror(code)) > 0
     assert b"unknown" in lib.pkv_strerror(12345)
 
@@ -116,6 +117,35 @@ def test_varlen_validation(lib):
     assert varlen(lib, to=None) == EWS
     assert varlen(lib, ml=None, dtype=0, D=64) == EWS     # required on every path
     assert varlen(lib, T=1 << 24, Hq=64, Hkv=8) == EUNSUP  # (row, head) waves beyond 2^26
+
+
+EHOST = -7
+
+
+def test_block_move_validation(lib):
+    arr = ctypes.c_void_p * 2
+    kp, vp = arr(16, 32), arr(48, 64)
+    nul = arr(16, None)
+    f = lib.paged_kv_copy_blocks
+    assert f(kp, vp, 2, P, 3, 10, 2, 16, 128, 9, None) == EDTYPE
+    assert f(kp, vp, 2, P, -1, 10, 2, 16, 128, 2, None) == ESHAPE
+    assert f(kp, vp, 2, P, 3, 0, 2, 16, 128, 2, None) == ESHAPE
+    assert f(kp, vp, -1, P, 3, 10, 2, 16, 128, 2, None) == ESHAPE
+    assert f(kp, vp, 2, P, 0, 10, 2, 16, 128, 2, None) == OK      # no-op
+    assert f(kp, vp, 0, P, 3, 10, 2, 16, 128, 2, None) == OK
+    assert f(kp, nul, 2, P, 3, 10, 2, 16, 128, 2, None) == ENULL
+    assert f(None, vp, 2, P, 3, 10, 2, 16, 128, 2, None) == ENULL
+    assert f(kp, vp, 2, None, 3, 10, 2, 16, 128, 2, None) == ENULL
+    assert f(kp, vp, 2, P, 1 << 24, 10, 2, 16, 128, 2, None) == EUNSUP
+    for g in (lib.paged_kv_swap_out, lib.paged_kv_swap_in):
+        slab = 2 * 16 * 128 * 2
+        assert g(P, 10 ** 9, kp, vp, 2, P, 3, 10, 2, 16, 128, 7, None) == EDTYPE
+        assert g(P, 10 ** 9, kp, vp, 2, P, 0, 10, 2, 16, 128, 2, None) == OK
+        assert g(None, 10 ** 9, kp, vp, 2, P, 3, 10, 2, 16, 128, 2, None) == ENULL
+        assert g(P, 10 ** 9, kp, vp, 2, None, 3, 10, 2, 16, 128, 2, None) == ENULL
+        # 2 layers x K/V x 3 ids x slab bytes are needed: one byte short is refused
+        assert g(P, 2 * 2 * 3 * slab - 1, kp, vp, 2, P, 3, 10, 2, 16, 128, 2, None) == EHOST
+        assert g(P, -5, kp, vp, 2, P, 3, 10, 2, 16, 128, 2, None) == EHOST
 
 
 def test_reduce_validation(lib):

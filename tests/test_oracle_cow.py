@@ -205,3 +205,28 @@ def test_copy_blocks_definition():
         copy_blocks(pool, [(1, 7), (2, 7)])
     with pytest.raises(AssertionError):
         copy_blocks(pool, [(1, 7), (7, 3)])
+
+
+def test_cow_workload_is_what_the_allocator_decides():
+    """The parallel-sampling workload's copies, slots and tables are exactly
+    what the oracle allocator's fork + append rule produces."""
+    import workloads as W
+    b = W.cow_fork_bf16(num_prompts=40, lo=1, hi=300, num_layers=1)
+    a = A.BlockAllocator(b.num_blocks, b.block_size, b.free_order.tolist())
+    for p, L in enumerate(b.prompt_lens):
+        a.add(("p", p), int(L))
+        for j in range(1, b.branches):
+            a.fork(("p", p), ("b", p, j))
+    pairs, slots = [], []
+    for p in range(len(b.prompt_lens)):
+        for j in list(range(1, b.branches)) + [0]:
+            slot, cp = a.append_slot(("b", p, j) if j else ("p", p))
+            slots.append(slot)
+            if cp:
+                pairs.append(cp)
+    assert pairs == [tuple(x) for x in b.copy_pairs.tolist()]
+    assert slots == b.slots.tolist()
+    for s, rid in enumerate(b.rids):
+        t = a.tables[rid]
+        assert t == b.block_table[s, :len(t)].tolist()
+        assert (b.block_table[s, len(t):] == -1).all()

@@ -67,6 +67,13 @@ class Batch:
     page_example: bool = False       # tensors come from the glossary page's recipe
     query_lens: np.ndarray | None = None  # int32 [S]: query tokens per sequence (multi-token
                                           # queries at the last positions), or None (one each)
+    # parallel sampling (copy-on-write): prompts, branches per prompt, the
+    # sequences' ids, the (src, dst) block copies and the new tokens' slots
+    prompt_lens: np.ndarray | None = None
+    branches: int = 1
+    rids: list | None = None
+    copy_pairs: np.ndarray | None = None
+    slots: np.ndarray | None = None
 
     @property
     def num_seqs(self) -> int:
@@ -283,6 +290,64 @@ def mixed_prefill_bf16(num_decode: int = 504, num_prefill: int = 8, chunk: int =
                         rng=rng)
 
 
+def cow_fork_bf16(num_prompts: int = 128, branches: int = 4, lo: int = 64, hi: int = 4096,
+                  num_layers: int = 32, seed: int = 1008, block_size: int = 16) -> Batch:
+    """Parallel sampling in the decode-step geometry (bf16, Hq=32, Hkv=8,
+    D=128, B=16, 32 layers): ``num_prompts`` prompts of U{lo..hi} tokens, each
+    forked into ``branches`` sequences sharing its blocks; then every branch
+    appends one token, prompt by prompt, the forked branches first and the
+    original last.
+
+    The situation, as input data: a prompt whose last block is partly filled
+    has that block shared by all its branches, so each forked branch gets the
+    next block of the free list as a copy of it, and the original, left the
+    sole owner, writes in place; a prompt whose last block is full gives every
+    branch a fresh block and no copy. Sequences are ordered prompt by prompt,
+    forked branches first."""
+    b = block_size
+    rng = np.random.default_rng(seed)
+    plens = rng.integers(lo, hi, size=num_prompts, endpoint=True).astype(np.int64)
+    need = int(sum(_nblocks(n, b) for n in plens)) + num_prompts * branches
+    n_blocks = max(1, math.ceil(1.1 * need))
+    free_order = rng.permutation(n_blocks).astype(np.int32)
+    ptab, pos = deal_tables(plens, b, free_order)
+    rows, lens, positions, slots, pairs, rids = [], [], [], [], [], []
+    for p in range(num_prompts):
+        L = int(plens[p])
+        nb = _nblocks(L, b)
+        base = [int(x) for x in ptab[p, :nb]]
+        for j in list(range(1, branches)) + [0]:
+            row = list(base)
+            if L % b == 0:
+                row.append(int(free_order[pos]))
+                pos += 1
+                slot = row[-1] * b
+            elif j != 0:
+                fresh = int(free_order[pos])
+                pos += 1
+                pairs.append((row[-1], fresh))
+                row[-1] = fresh
+                slot = fresh * b + L % b
+            else:
+                slot = row[-1] * b + L % b
+            rows.append(row)
+            lens.append(L + 1)
+            positions.append(L)
+            slots.append(slot)
+            rids.append(("b", p, j) if j else ("p", p))
+    width = max(len(r) for r in rows)
+    table = np.full((len(rows), width), -1, np.int32)
+    for s, r in enumerate(rows):
+        table[s, :len(r)] = r
+    return Batch(name="cow_fork_bf16", dtype="bf16", num_heads=32, num_kv_heads=8,
+                 head_size=128, block_size=b, num_blocks=n_blocks, block_table=table,
+                 context_lens=np.array(lens, np.int32), free_order=free_order, seed=seed,
+                 num_layers=num_layers, positions=np.array(positions, np.int32),
+                 prompt_lens=plens.astype(np.int32), branches=branches, rids=rids,
+                 copy_pairs=np.array(pairs, np.int64).reshape(-1, 2),
+                 slots=np.array(slots, np.int64))
+
+
 CASES = {
     "tiny": tiny_page_example,
     "mha_fp16": mha_fp16,
@@ -291,6 +356,7 @@ CASES = {
     "decode_step_bf16": decode_step_bf16,
     "spec_verify_bf16": spec_verify_bf16,
     "mixed_prefill_bf16": mixed_prefill_bf16,
+    "cow_fork_bf16": cow_fork_bf16,
 }
 
 
