@@ -11,6 +11,14 @@ one step is one paged_varlen_attention call (balanced split kernel over
 (sequence, column group) units, then the merge over query rows) on one layer,
 with L2/MALL evicted before it.
 
+Block moves: ``--workload cow_fork_bf16`` times paged_kv_copy_blocks over
+all 32 layers of a parallel-sampling fork (128 prompts x 4 branches, one copy
+per forked branch whose prompt ends in a partly filled block);
+``--workload swap_bf16`` times paged_kv_swap_out / paged_kv_swap_in of 8
+sequences' blocks of the 32-layer decode step through pinned host memory.
+Each is set beside a plain contiguous copy of the same bytes (device copy,
+or torch's host copies) measured in the same run.
+
 Prints one JSON line. `value` is KV-read GB/s over the whole step: the
 algorithmic bytes every layer must read (2 * Hkv * D * 2 B per live
 (sequence, position)) divided by the step time. The `roofline` object is for
@@ -37,25 +45,27 @@ METRIC = "paged decode KV-read HBM GB/s (% of MI355X peak) + decoded seqs·token
 HBM_PEAK_GBS = 8000.0
 DECODE_SOURCES = ["paged_kv_cache_113_amd/csrc/decode_fast.hip",
                   "paged_kv_cache_113_amd/csrc/device.h"]
+MOVE_SOURCES = ["paged_kv_cache_113_amd/csrc/block_ops.hip",
+                "paged_kv_cache_113_amd/csrc/device.h"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=DECODE_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in DECODE_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str, kernel_bytes_per_launch: float):
-    """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, or None when it is missing or the kernel changed since."""
-    path = os.path.join(ROOT, "profiles", f"decode_split_{workload}_traffic.json")
+def traffic_for(workload: str, kernel: str = "decode_split", sources=DECODE_SOURCES):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -81,6 +91,145 @@ def default_partition(workload):
 
 
 VARLEN = ("spec_verify_bf16", "mixed_prefill_bf16")
+BLOCK_MOVES = ("cow_fork_bf16", "swap_bf16")
+PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def _events_ms(fn, reps, flush=None):
+    """Mean and spread of fn's device time over ``reps`` runs (HIP events on
+    torch's current stream), with an optional cache-evicting read before each."""
+    import torch
+    xs = []
+    for _ in range(reps):
+        if flush is not None:
+            flush.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        xs.append(e0.elapsed_time(e1))
+    return float(np.mean(xs)), float(np.percentile(xs, 10)), float(np.percentile(xs, 90))
+
+
+def bench_block_moves(args):
+    import torch
+    import paged_kv_cache_113_amd as pkv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    steps, warm = args.steps, args.warmup
+    if args.workload == "cow_fork_bf16":
+        b = W.cow_fork_bf16()
+    else:
+        b = W.decode_step_bf16()
+    L = b.num_layers
+    t0 = time.perf_counter()
+    ks, vs = [], []
+    for l in range(L):
+        t = W.layer_tensors(b, layer=l, device=dev, poison=False)
+        ks.append(t["k_cache"])
+        vs.append(t["v_cache"])
+        del t
+    torch.cuda.synchronize()
+    print(f"[bench] {args.workload}: {L} layers x {b.num_blocks} blocks generated in "
+          f"{time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    slab = b.num_kv_heads * b.block_size * b.head_size * 2
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    pools = pkv.PoolSet(ks, vs)     # checked once: the timed calls only launch
+    config = {"workload": args.workload, "layers": L, "num_kv_heads": b.num_kv_heads,
+              "block_size": b.block_size, "head_size": b.head_size,
+              "slab_bytes": slab, "blocks_per_layer": b.num_blocks}
+    line = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": b.dtype,
+            "data": "synthetic", "cpu_baseline": None}
+    if args.workload == "cow_fork_bf16":
+        pairs = torch.as_tensor(b.copy_pairs, dtype=torch.int64, device=dev)
+        n = int(pairs.shape[0])
+        run = lambda: pkv.paged_kv_copy_blocks(pools, None, pairs)   # noqa: E731
+        for _ in range(warm):
+            run()
+        ms, p10, p90 = _events_ms(run, steps, flush)
+        moved = 2.0 * n * L * 2 * slab               # K and V, read + write, per pair
+        # a source shared by several pairs (the branches of one prompt) needs
+        # reading once: the algorithmic bytes count it once
+        n_src = len(set(int(x) for x in b.copy_pairs[:, 0]))
+        unique = float(n_src + n) * L * 2 * slab
+        # the same bytes as one contiguous device copy
+        a = torch.empty(n * L * 2 * slab // 2, dtype=torch.bfloat16, device=dev)
+        c = torch.empty_like(a)
+        for _ in range(warm):
+            c.copy_(a)
+        cms = _events_ms(lambda: c.copy_(a), steps, flush)[0]
+        del a, c
+        achieved = unique / (ms / 1e3) / 1e9
+        config.update({"pairs": n, "distinct_sources": n_src, "branches": b.branches,
+                       "prompts": len(b.prompt_lens)})
+        line.update({
+            "value": round(achieved, 2), "ms_per_step": round(ms, 4), "config": config,
+            "kernels_ms": {"copy_blocks_avg": round(ms, 4), "copy_blocks_p10": round(p10, 4),
+                           "copy_blocks_p90": round(p90, 4),
+                           "contiguous_copy_same_bytes": round(cms, 4)},
+            "blocks_per_s": round(n * L / (ms / 1e3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_for(args.workload, "move_blocks", MOVE_SOURCES),
+                         "kernel": "move_blocks_kernel<16, copy>",
+                         "bytes_per_launch": unique, "logical_bytes_per_launch": moved,
+                         "logical_gbs": round(moved / (ms / 1e3) / 1e9, 2),
+                         "contiguous_copy_gbs": round(moved / (cms / 1e3) / 1e9, 2)}})
+    else:
+        rng = np.random.default_rng(17)
+        victims = np.sort(rng.choice(b.num_seqs, 8, replace=False))
+        ids = [int(x) for s in victims for x in b.block_table[s] if x >= 0]
+        keep = set(int(x) for s in range(b.num_seqs) if s not in set(victims.tolist())
+                   for x in b.block_table[s] if x >= 0)
+        free = np.array([x for x in range(b.num_blocks) if x not in keep], np.int64)
+        fresh = rng.permutation(free)[:len(ids)]
+        n = len(ids)
+        ids_t = torch.as_tensor(ids, dtype=torch.int64, device=dev)
+        fresh_t = torch.as_tensor(fresh, dtype=torch.int64, device=dev)
+        buf = torch.empty((L, 2, n, b.num_kv_heads, b.block_size, b.head_size),
+                          dtype=torch.bfloat16, pin_memory=True)
+        out_fn = lambda: pkv.paged_kv_swap_out(buf, pools, None, ids_t)   # noqa: E731
+        in_fn = lambda: pkv.paged_kv_swap_in(buf, pools, None, fresh_t)   # noqa: E731
+        for _ in range(warm):
+            out_fn()
+            in_fn()
+        o_ms, o10, o90 = _events_ms(out_fn, steps)
+        i_ms, i10, i90 = _events_ms(in_fn, steps)
+        moved = float(n) * L * 2 * slab
+        d = torch.empty(buf.shape, dtype=torch.bfloat16, device=dev)
+        for _ in range(warm):
+            buf.copy_(d, non_blocking=True)
+            d.copy_(buf, non_blocking=True)
+        d2h = _events_ms(lambda: buf.copy_(d, non_blocking=True), steps)[0]
+        h2d = _events_ms(lambda: d.copy_(buf, non_blocking=True), steps)[0]
+        del d
+        out_gbs = moved / (o_ms / 1e3) / 1e9
+        in_gbs = moved / (i_ms / 1e3) / 1e9
+        config.update({"swapped_sequences": int(len(victims)), "blocks": n,
+                       "tokens": int(b.context_lens[victims].sum())})
+        line.update({
+            "value": round(moved * 2 / ((o_ms + i_ms) / 1e3) / 1e9, 2),
+            "ms_per_step": round(o_ms + i_ms, 4), "config": config,
+            "kernels_ms": {"swap_out_avg": round(o_ms, 4), "swap_out_p10": round(o10, 4),
+                           "swap_out_p90": round(o90, 4), "swap_in_avg": round(i_ms, 4),
+                           "swap_in_p10": round(i10, 4), "swap_in_p90": round(i90, 4),
+                           "torch_d2h_same_bytes": round(d2h, 4),
+                           "torch_h2d_same_bytes": round(h2d, 4)},
+            "roofline": {"bound": "pcie", "achieved": round(out_gbs, 2), "peak": PCIE_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(out_gbs / PCIE_PEAK_GBS, 4),
+                         "traffic": None, "kernel": "move_blocks_kernel<16, swap out>",
+                         "bytes_per_launch": moved,
+                         "swap_in_gbs": round(in_gbs, 2),
+                         "swap_in_frac": round(in_gbs / PCIE_PEAK_GBS, 4),
+                         "torch_d2h_gbs": round(moved / (d2h / 1e3) / 1e9, 2),
+                         "torch_h2d_gbs": round(moved / (h2d / 1e3) / 1e9, 2)}})
+    line["pct_of_peak"] = round(100.0 * line["roofline"]["frac"], 2)
+    print(json.dumps(line), flush=True)
 
 
 def visible_pairs(batch) -> np.ndarray:
@@ -166,7 +315,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode_step_bf16",
                     choices=["decode_step_bf16", "mha_fp16", "gqa_shared_bf16",
-                             "long_split_bf16", *VARLEN])
+                             "long_split_bf16", *VARLEN, *BLOCK_MOVES])
     ap.add_argument("--max-partitions", type=int, default=8,
                     help="multi-token workloads: pieces per query row at most")
     ap.add_argument("--partition-size", type=int, default=None)
@@ -186,6 +335,10 @@ def main():
               "(sequences and KV heads shard with no communication; see DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in BLOCK_MOVES:
+        bench_block_moves(args)
+        return
 
     import torch
     import paged_kv_cache_113_amd as pkv
@@ -333,7 +486,7 @@ def main():
     value = step_bytes / (ms_per_step / 1e3) / 1e9
     achieved = layer_bytes / (dec_ms / 1e3) / 1e9
     positions = float(np.sum(batch.context_lens, dtype=np.int64))
-    traffic = traffic_for(args.workload, layer_bytes)
+    traffic = traffic_for(args.workload)
     pairs = float(visible_pairs(batch).sum()) if varlen else positions
     flops = 4.0 * batch.num_heads * batch.head_size * pairs   # q.K and P.V, per layer
 

@@ -153,33 +153,49 @@ def paged_varlen_attention(out, query, k_cache, v_cache, block_table, query_star
         _ptr(tmp_out), _DTYPE[query.dtype], _stream(stream)))
 
 
-def _pool_ptrs(k_caches, v_caches):
-    """Host arrays of the layers' pool pointers, and the shared geometry."""
-    if len(k_caches) != len(v_caches) or not k_caches:
-        raise ValueError("one K and one V pool per layer")
-    _dev(*k_caches, *v_caches)
-    shape, dtype = k_caches[0].shape, k_caches[0].dtype
-    for t in (*k_caches, *v_caches):
-        if t.shape != shape or t.dtype != dtype:
-            raise ValueError("every layer's pools share one shape and dtype")
-    arr = (ctypes.c_void_p * len(k_caches))
-    kp = arr(*[t.data_ptr() for t in k_caches])
-    vp = arr(*[t.data_ptr() for t in v_caches])
-    return kp, vp, shape, dtype
+class PoolSet:
+    """Every layer's K and V pools, checked once (one shape and dtype, on the
+    GPU, contiguous), with the host arrays of their device pointers that the
+    block-move calls take. Pass it in place of the two lists to skip the
+    per-call checks in a serving loop."""
+
+    def __init__(self, k_caches, v_caches):
+        if isinstance(k_caches, PoolSet):
+            raise TypeError("already a PoolSet")
+        if len(k_caches) != len(v_caches) or not k_caches:
+            raise ValueError("one K and one V pool per layer")
+        _dev(*k_caches, *v_caches)
+        shape, dtype = k_caches[0].shape, k_caches[0].dtype
+        for t in (*k_caches, *v_caches):
+            if t.shape != shape or t.dtype != dtype:
+                raise ValueError("every layer's pools share one shape and dtype")
+        arr = ctypes.c_void_p * len(k_caches)
+        self.k = arr(*[t.data_ptr() for t in k_caches])
+        self.v = arr(*[t.data_ptr() for t in v_caches])
+        self.tensors = (list(k_caches), list(v_caches))   # keeps the storage alive
+        self.num_layers = len(k_caches)
+        self.shape = shape
+        self.dtype = dtype
+
+
+def _pools(k_caches, v_caches):
+    ps = k_caches if isinstance(k_caches, PoolSet) else PoolSet(k_caches, v_caches)
+    return ps.k, ps.v, ps.num_layers, ps.shape, ps.dtype
 
 
 def paged_kv_copy_blocks(k_caches, v_caches, block_mapping, stream=None):
     """Copy block src -> dst in every layer's K and V pool, for each row
-    (src, dst) of block_mapping [n, 2] int64 (copy-on-write)."""
-    kp, vp, (n, hkv, b, d), dtype = _pool_ptrs(k_caches, v_caches)
+    (src, dst) of block_mapping [n, 2] int64 (copy-on-write). k_caches may be
+    a PoolSet (then v_caches is ignored)."""
+    kp, vp, nl, (n, hkv, b, d), dtype = _pools(k_caches, v_caches)
     _dev(block_mapping)
     assert block_mapping.dtype == torch.int64 and block_mapping.shape[-1] == 2
     _check("paged_kv_copy_blocks", lib.paged_kv_copy_blocks(
-        kp, vp, len(k_caches), _ptr(block_mapping), block_mapping.shape[0], n, hkv, b, d,
+        kp, vp, nl, _ptr(block_mapping), block_mapping.shape[0], n, hkv, b, d,
         _DTYPE[dtype], _stream(stream)))
 
 
-def _host_buf(host, n_layers, n_ids, shape, dtype):
+def _host_buf(host, dtype):
     if host.is_cuda or not host.is_contiguous() or host.dtype != dtype:
         raise ValueError("the host buffer is a contiguous CPU tensor of the pools' dtype")
     return ctypes.c_void_p(host.data_ptr()), host.numel() * host.element_size()
@@ -187,24 +203,25 @@ def _host_buf(host, n_layers, n_ids, shape, dtype):
 
 def paged_kv_swap_out(host_dst, k_caches, v_caches, block_ids, stream=None):
     """host_dst [L, 2, n, Hkv, B, D] (pinned) <- blocks block_ids of every
-    layer's K (index 0) and V (index 1) pool."""
-    kp, vp, (n, hkv, b, d), dtype = _pool_ptrs(k_caches, v_caches)
+    layer's K (index 0) and V (index 1) pool. k_caches may be a PoolSet."""
+    kp, vp, nl, (n, hkv, b, d), dtype = _pools(k_caches, v_caches)
     _dev(block_ids)
     assert block_ids.dtype == torch.int64
-    hp, nbytes = _host_buf(host_dst, len(k_caches), block_ids.numel(), (hkv, b, d), dtype)
+    hp, nbytes = _host_buf(host_dst, dtype)
     _check("paged_kv_swap_out", lib.paged_kv_swap_out(
-        hp, nbytes, kp, vp, len(k_caches), _ptr(block_ids), block_ids.numel(), n, hkv, b, d,
+        hp, nbytes, kp, vp, nl, _ptr(block_ids), block_ids.numel(), n, hkv, b, d,
         _DTYPE[dtype], _stream(stream)))
 
 
 def paged_kv_swap_in(host_src, k_caches, v_caches, block_ids, stream=None):
-    """Blocks block_ids of every layer's pools <- host_src [L, 2, n, Hkv, B, D]."""
-    kp, vp, (n, hkv, b, d), dtype = _pool_ptrs(k_caches, v_caches)
+    """Blocks block_ids of every layer's pools <- host_src [L, 2, n, Hkv, B, D].
+    k_caches may be a PoolSet."""
+    kp, vp, nl, (n, hkv, b, d), dtype = _pools(k_caches, v_caches)
     _dev(block_ids)
     assert block_ids.dtype == torch.int64
-    hp, nbytes = _host_buf(host_src, len(k_caches), block_ids.numel(), (hkv, b, d), dtype)
+    hp, nbytes = _host_buf(host_src, dtype)
     _check("paged_kv_swap_in", lib.paged_kv_swap_in(
-        hp, nbytes, kp, vp, len(k_caches), _ptr(block_ids), block_ids.numel(), n, hkv, b, d,
+        hp, nbytes, kp, vp, nl, _ptr(block_ids), block_ids.numel(), n, hkv, b, d,
         _DTYPE[dtype], _stream(stream)))
 
 

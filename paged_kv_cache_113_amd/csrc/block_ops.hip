@@ -26,9 +26,13 @@ namespace {
 constexpr int kMoveThreads = 256;
 constexpr int kUnroll = 8;
 
+// Copy units are clang vector types: an array of them stays in registers
+// (an array of HIP's struct vectors would be staged through scratch memory).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <int W> struct Unit;
-template <> struct Unit<16> { using type = uint4; };
-template <> struct Unit<8> { using type = uint2; };
+template <> struct Unit<16> { using type = u32x4; };
+template <> struct Unit<8> { using type = u32x2; };
 template <> struct Unit<4> { using type = uint32_t; };
 template <> struct Unit<2> { using type = uint16_t; };
 
@@ -70,19 +74,18 @@ __global__ __launch_bounds__(kMoveThreads) void move_blocks_kernel(
   const int64_t units = slab_bytes / W;
   const T* __restrict__ s = reinterpret_cast<const T*>(src);
   T* __restrict__ d = reinterpret_cast<T*>(dst);
-  for (int64_t u0 = threadIdx.x; u0 < units; u0 += kMoveThreads * kUnroll) {
+  // whole batches of kUnroll chunks per lane: no per-chunk guard, so all the
+  // loads of a batch are issued before the first one is waited for
+  constexpr int kBatch = kMoveThreads * kUnroll;
+  const int64_t whole = units / kBatch * kBatch;
+  for (int64_t u0 = threadIdx.x; u0 < whole; u0 += kBatch) {
     T r[kUnroll];
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int64_t u = u0 + k * kMoveThreads;
-      if (u < units) r[k] = s[u];
-    }
+    for (int k = 0; k < kUnroll; ++k) r[k] = s[u0 + k * kMoveThreads];
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int64_t u = u0 + k * kMoveThreads;
-      if (u < units) d[u] = r[k];
-    }
+    for (int k = 0; k < kUnroll; ++k) d[u0 + k * kMoveThreads] = r[k];
   }
+  for (int64_t u = whole + threadIdx.x; u < units; u += kMoveThreads) d[u] = s[u];
 }
 
 int unit_width(int64_t slab_bytes, uintptr_t addr_bits) {

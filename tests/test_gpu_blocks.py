@@ -71,7 +71,8 @@ def test_copy_blocks_many_layers(dev, pkv):
     ks, vs = _pools(70, (6, 2, 16, 16), "bf16", dev, 12)
     before = [(_raw(k, "bf16"), _raw(v, "bf16")) for k, v in zip(ks, vs)]
     pairs = [(0, 5), (2, 3)]
-    pkv.paged_kv_copy_blocks(ks, vs, torch.as_tensor(pairs, dtype=torch.int64, device=dev))
+    pools = pkv.PoolSet(ks, vs)      # checked once, reused
+    pkv.paged_kv_copy_blocks(pools, None, torch.as_tensor(pairs, dtype=torch.int64, device=dev))
     torch.cuda.synchronize()
     for (k0, v0), k, v in zip(before, ks, vs):
         assert np.array_equal(_raw(k, "bf16"), oracle.scatter.copy_blocks(k0, pairs))
