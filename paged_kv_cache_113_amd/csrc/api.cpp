@@ -218,7 +218,10 @@ int paged_varlen_attention(float* out, const void* query, const void* k_cache,
   a.num_tokens = num_tokens;
   if (!pkv::fast_varlen_supported(a))
     return launch_status(pkv::launch_varlen_generic(a, as_stream(stream)));
+  // sequences with short query sets, then those with long chunks (each
+  // kernel takes its own kind), then the merge of all query rows
   hipError_t e = pkv::launch_varlen_fast(a, as_stream(stream));
+  if (e == hipSuccess) e = pkv::launch_prefill_fast(a, as_stream(stream));
   if (e != hipSuccess) return PKV_ERR_LAUNCH;
   return launch_status(pkv::launch_reduce(out, max_logits, exp_sums, tmp_out, nullptr,
                                           num_tokens, num_heads, head_size, 1, max_partitions,

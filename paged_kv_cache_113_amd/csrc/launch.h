@@ -56,6 +56,9 @@ hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
 // merge; same shapes as the decode fast path.
 bool fast_varlen_supported(const DecodeArgs& a);
 hipError_t launch_varlen_fast(const DecodeArgs& a, hipStream_t stream);
+// Long chunks (at least 128 (token, head) columns per KV head): workgroups
+// share each K/V tile in LDS among 128 columns; partials for the merge.
+hipError_t launch_prefill_fast(const DecodeArgs& a, hipStream_t stream);
 // Plain path: one wave per (query row, head), output written directly.
 hipError_t launch_varlen_generic(const DecodeArgs& a, hipStream_t stream);
 

@@ -1,0 +1,534 @@
+// Multi-token queries over paged KV, long chunks (chunked prefill): the
+// prefill kernel for gfx950.
+//
+// What it computes is the causal attention of paged_varlen_attention: token
+// i of a sequence with ctx positions and q_s query tokens sits at position
+// ctx - q_s + i and attends positions 0 .. ctx - q_s + i, softmax(scale q K^T)
+// V over K/V rows found through the block table ("vLLM PagedAttention: from
+// fragmentation to slot mapping", sections 3 and 7; a step mixing prefill
+// chunks and decode tokens: "vLLM source walkthrough: PagedAttention and
+// continuous batching", section 2.8).
+//
+// It takes the sequences whose query tokens fill at least kPrefillCols
+// (token, head) columns per KV head. There q.K^T is a real dense contraction
+// and the cost is in the matrix cores and in re-reading K/V, so a workgroup
+// of 4 waves loads each 64-position stage of K and V once into LDS and all
+// 4 waves use it, each for 2 groups of 16 columns (128 columns per stage):
+//  * unit = (sequence, 8 column groups of 16/G tokens x G heads); wave w owns
+//    groups 2w and 2w + 1 of the unit;
+//  * a stage's K rows sit in LDS at a 272 B pitch (the 16 rows of an
+//    A-operand read start 4 banks apart), its V rows at a 288 B pitch that
+//    ds_read_b64_tr_b16 turns into V^T; one LDS buffer, the next stage's
+//    global loads held in registers during this stage's math, two barriers
+//    per stage;
+//  * per 32 positions and group: scores of two 16-position blocks on
+//    v_mfma_f32_16x16x32 (lane (col n, group j) gets positions 4j..4j+3 of
+//    each block), one online-softmax step over those 8 positions, and P.V on
+//    v_mfma_f32_16x16x32 with k running over exactly those 8 positions per
+//    lane: the lane's own probabilities are the P^T operand (a 16-bit high
+//    part and the rounding of the remainder), and two transposed reads of the
+//    two 16-row halves give the V^T operand, shared by both groups. The
+//    accumulators are rescaled only when some column's running max moved;
+//  * work split: for each KV head the stream of all units' stages is cut into
+//    equal ranges, one per workgroup (the decode kernel's balanced split at
+//    workgroup granularity); a range ends a piece wherever a unit or the
+//    range ends, and the reduce kernel merges the pieces.
+#include <atomic>
+#include <type_traits>
+
+#include "device.h"
+#include "launch.h"
+#include "mfma_tile.h"
+#include "varlen.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kPfThreads = 256;
+constexpr int kPfWaves = kPfThreads / 64;
+constexpr int kGroupsPerWave = 2;                          // 2 x 16 columns
+constexpr int kGroupsPerUnit = kPfWaves * kGroupsPerWave;  // 128 columns
+constexpr int kStage = 64;                                 // positions per stage
+constexpr int kSub = kStage / kTile;                       // 16-row blocks per stage
+constexpr int kKRow = kD * 2 + 16;                         // K row pitch in LDS
+constexpr int kMaxSeqsPrefill = 8192;                      // LDS prefix capacity
+constexpr int kXcdCount = 8;                               // MI355X: 8 XCDs
+
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// s_waitcnt vmcnt(0): every vector memory load issued so far has arrived.
+__device__ __forceinline__ void wait_all_loads() {
+  // gfx9 encoding: vmcnt [3:0] and [15:14] = 0, expcnt [6:4] and lgkmcnt
+  // [11:8] at their maxima (not waited for)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// 8 probabilities in [0, 1] as 16-bit high parts and the 16-bit roundings of
+// the remainders, packed in k order (a 16x16x32 operand).
+template <typename T>
+__device__ __forceinline__ void split_p8(const float* p, uint4& hi, uint4& lo) {
+  uint2 h0, l0, h1, l1;
+  split_p<T>(p, h0, l0);
+  split_p<T>(p + 4, h1, l1);
+  hi = make_uint4(h0.x, h0.y, h1.x, h1.y);
+  lo = make_uint4(l0.x, l0.y, l1.x, l1.y);
+}
+
+// A stage of the per-KV-head stream: stage t of the n stages of unit (s, u).
+struct PfCursor {
+  int s, u, nu, t, n, ctx, q0, qn;
+};
+
+// Stages a group of query tokens [u*per, min((u+1)*per, qn)) reads: what its
+// last token sees, in 64-position stages, at least one.
+__device__ __forceinline__ int unit_stages(int ctx, int qn, int u, int per) {
+  const int e = (u + 1) * per < qn ? (u + 1) * per : qn;
+  const int vis = ctx - qn + e;
+  const int n = vis > 0 ? (vis + kStage - 1) / kStage : 0;
+  return n > 0 ? n : 1;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a, int wgs_per_kv) {
+  extern __shared__ int s_pre[];  // [S + 1]: stages of units before sequence s
+  __shared__ __attribute__((aligned(16))) char s_k[kStage * kKRow];
+  __shared__ __attribute__((aligned(16))) char s_v[kStage * kSlotRow];
+  __shared__ int s_max[kPfWaves];
+  __shared__ int s_wsum[kPfWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int S = a.num_seqs;
+  const int G = a.num_heads / a.num_kv_heads;
+  const int mp = a.max_partitions;
+  const int cap = a.max_blocks * a.block_size;
+  const int tpg = kTile / G;                // query tokens per column group
+  const int utok = kGroupsPerUnit * tpg;    // query tokens per unit
+
+  auto seq_ctx = [&](int s) {
+    int c = read_only(a.context_lens + s);
+    return c < cap ? c : cap;
+  };
+  auto units_of = [&](int qn) { return prefill_sized(qn, G) ? (qn + utok - 1) / utok : 0; };
+  auto seq_stages = [&](int s, int& last) {
+    const int ctx = seq_ctx(s);
+    int q0, qn;
+    query_rows(a, s, q0, qn);
+    const int nu = units_of(qn);
+    int tot = 0;
+    last = 0;
+    for (int u = 0; u < nu; ++u) {
+      last = unit_stages(ctx, qn, u, utok);
+      tot += last;
+    }
+    return tot;
+  };
+
+  // 1. stages per sequence and their exclusive prefix (every workgroup
+  //    builds the same table)
+  const int per = (S + kPfThreads - 1) / kPfThreads;
+  const int s_lo = tid * per;
+  int local = 0, nmax = 0;
+  for (int i = 0; i < per; ++i) {
+    const int s = s_lo + i;
+    if (s < S) {
+      int last;
+      local += seq_stages(s, last);
+      nmax = last > nmax ? last : nmax;
+    }
+  }
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  const int wave_total = __shfl(incl, 63, 64);
+  int wmax = nmax;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int y = __shfl_xor(wmax, off, 64);
+    wmax = y > wmax ? y : wmax;
+  }
+  if (lane == 0) {
+    s_wsum[w] = wave_total;
+    s_max[w] = wmax;
+  }
+  __syncthreads();
+  int base = 0, T1 = 0, n_max = 0;
+#pragma unroll
+  for (int i = 0; i < kPfWaves; ++i) {
+    base += i < w ? s_wsum[i] : 0;
+    T1 += s_wsum[i];
+    n_max = s_max[i] > n_max ? s_max[i] : n_max;
+  }
+  {
+    int run = base + incl - local;
+    for (int i = 0; i < per; ++i) {
+      const int s = s_lo + i;
+      if (s < S) {
+        s_pre[s] = run;
+        int last;
+        run += seq_stages(s, last);
+      }
+    }
+    if (tid == 0) s_pre[S] = T1;
+  }
+  __syncthreads();
+  T1 = __builtin_amdgcn_readfirstlane(T1);
+  if (T1 == 0) return;
+
+  // 2. this workgroup's KV head and range (workgroups numbered XCD by XCD:
+  //    one XCD streams a contiguous run of ranges over all KV heads)
+  const int n_wg = gridDim.x;
+  const int xcd_rank = (blockIdx.x % kXcdCount) * (n_wg / kXcdCount) + blockIdx.x / kXcdCount;
+  const int wg_rank = n_wg % kXcdCount == 0 ? xcd_rank : static_cast<int>(blockIdx.x);
+  const int kvh = wg_rank % a.num_kv_heads;
+  const int k = wg_rank / a.num_kv_heads;
+  int64_t Wk = wgs_per_kv;
+  n_max = __builtin_amdgcn_readfirstlane(n_max);
+  if (mp >= 2) {
+    const int q_min = n_max > 1 ? (n_max - 1 + mp - 2) / (mp - 1) : 1;
+    const int64_t lim = T1 / q_min;
+    Wk = Wk < lim ? Wk : lim;
+  } else {
+    Wk = 1;
+  }
+  Wk = Wk < 1 ? 1 : Wk;
+  if (k >= Wk) return;  // the whole workgroup: no barrier is left waiting
+  const int b0 = static_cast<int>(static_cast<int64_t>(k) * T1 / Wk);
+  const int b1 = static_cast<int>(static_cast<int64_t>(k + 1) * T1 / Wk);
+  const int len = b1 - b0;
+  auto range_of = [&](int x) {
+    return static_cast<int>(((static_cast<int64_t>(x) + 1) * Wk - 1) / T1);
+  };
+  auto pre = [&](int s) { return __builtin_amdgcn_readfirstlane(s_pre[s]); };
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre(mid) <= b0) lo = mid; else hi = mid - 1;
+  }
+  auto open_seq = [&](int s) {
+    PfCursor c;
+    c.s = s;
+    c.u = 0;
+    c.t = 0;
+    c.ctx = seq_ctx(s);
+    query_rows(a, s, c.q0, c.qn);
+    c.nu = units_of(c.qn);
+    c.n = unit_stages(c.ctx, c.qn, 0, utok);
+    return c;
+  };
+  PfCursor cur = open_seq(lo);
+  int ustart = pre(lo);
+  {
+    int x = b0 - ustart;
+    while (x >= cur.n && cur.u + 1 < cur.nu) {
+      x -= cur.n;
+      ustart += cur.n;
+      ++cur.u;
+      cur.n = unit_stages(cur.ctx, cur.qn, cur.u, utok);
+    }
+    cur.t = x;
+  }
+  int piece = k - range_of(ustart);
+  auto advance = [&](const PfCursor& c) {
+    PfCursor r = c;
+    if (c.t + 1 < c.n) {
+      r.t = c.t + 1;
+      return r;
+    }
+    if (c.u + 1 < c.nu) {
+      r.u = c.u + 1;
+      r.t = 0;
+      r.n = unit_stages(c.ctx, c.qn, r.u, utok);
+      return r;
+    }
+    int s = c.s + 1;
+    while (s < S - 1 && pre(s + 1) == pre(s)) ++s;  // sequences with no units here
+    return open_seq(s);
+  };
+
+  // this lane's two columns: group 2w + gi of the unit, token (within the
+  // unit) (2w + gi) * tpg + col / G, head col % G
+  const int my_head = col % G;
+  const bool my_col = col < tpg * G;
+  auto token_of = [&](const PfCursor& c, int gi) {
+    return c.u * utok + (kGroupsPerWave * w + gi) * tpg + col / G;
+  };
+  auto live = [&](const PfCursor& c, int gi) { return my_col && token_of(c, gi) < c.qn; };
+  // a group with no live column in the wave: its math is skipped (uniform)
+  auto group_live = [&](const PfCursor& c, int gi) {
+    return c.u * utok + (kGroupsPerWave * w + gi) * tpg < c.qn;
+  };
+
+  const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
+  const char* __restrict__ vc = static_cast<const char*>(a.v_cache);
+  const int64_t head_stride = static_cast<int64_t>(a.block_size) * kD * 2;
+  const int64_t block_stride = head_stride * a.num_kv_heads;
+  // loader lane: rows tid / 16 + 16 m (m < kSub) of the stage, chunk tid % 16
+  const int ld_row = tid >> 4;
+  const int ld_chunk = tid & 15;
+  auto row_of = [&](int s) { return a.block_table + static_cast<int64_t>(s) * a.max_blocks; };
+  // global loads of a stage's K and V rows for this lane; bit m of the
+  // result says whether 16-row block m has a table entry in the pool (if
+  // not, block 0 is read instead and its rows are masked)
+  auto load_stage = [&](const PfCursor& c, uint4* kr, uint4* vr) {
+    int ok = 0;
+#pragma unroll
+    for (int m = 0; m < kSub; ++m) {
+      const int tok0 = c.t * kStage + m * kTile;
+      const int64_t blk = physical_block(row_of(c.s), tok0, a.block_size, a.max_blocks,
+                                         a.num_blocks);
+      const int64_t off = (blk < 0 ? 0 : blk) * block_stride + kvh * head_stride +
+                          static_cast<int64_t>(tok0 % a.block_size + ld_row) * kD * 2 +
+                          ld_chunk * 16;
+      kr[m] = *reinterpret_cast<const uint4*>(kc + off);
+      vr[m] = *reinterpret_cast<const uint4*>(vc + off);
+      ok |= (blk >= 0) << m;
+    }
+    return ok;
+  };
+  // wave-uniform V limit: positions the unit's last token sees, from the stage
+  auto vlimit = [&](const PfCursor& c) {
+    const int e = (c.u + 1) * utok < c.qn ? (c.u + 1) * utok : c.qn;
+    return c.ctx - c.qn + e - c.t * kStage;
+  };
+
+  const float qk_scale = a.scale * kLog2e;
+  uint4 q[kGroupsPerWave][4];
+  auto load_q_unit = [&](const PfCursor& c) {
+#pragma unroll
+    for (int gi = 0; gi < kGroupsPerWave; ++gi) {
+      const bool ok = live(c, gi);
+      const char* qp = static_cast<const char*>(a.query) +
+                       ((static_cast<int64_t>(c.q0 + token_of(c, gi)) * a.num_heads +
+                         kvh * G + my_head) * kD) * 2;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        q[gi][kk] = ok ? *reinterpret_cast<const uint4*>(qp + (4 * kk + grp) * 16)
+                       : make_uint4(0, 0, 0, 0);
+    }
+  };
+  Attend<T> st[kGroupsPerWave];
+#pragma unroll
+  for (int gi = 0; gi < kGroupsPerWave; ++gi) st[gi].reset();
+
+  auto finish = [&](const PfCursor& c) {
+#pragma unroll
+    for (int gi = 0; gi < kGroupsPerWave; ++gi) {
+      const float l_col = st[gi].column_sum();
+      if (live(c, gi)) {
+        const int64_t prow = static_cast<int64_t>(c.q0 + token_of(c, gi)) * a.num_heads +
+                             kvh * G + my_head;
+        if (piece < mp) {
+          const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
+          float* dst = a.tmp_out + (prow * mp + piece) * kD + 4 * grp;
+#pragma unroll
+          for (int db = 0; db < 8; ++db)
+            *reinterpret_cast<float4*>(dst + 16 * db) =
+                make_float4(st[gi].acc[db][0] * inv, st[gi].acc[db][1] * inv,
+                            st[gi].acc[db][2] * inv, st[gi].acc[db][3] * inv);
+          if (grp == 0) {
+            a.max_logits[prow * mp + piece] = st[gi].m_run * kLn2;
+            a.exp_sums[prow * mp + piece] = l_col;
+          }
+        }
+        if (c.t == c.n - 1 && grp == 0) {
+          for (int p = piece + 1; p < mp; ++p) {
+            a.max_logits[prow * mp + p] = -INFINITY;
+            a.exp_sums[prow * mp + p] = 0.f;
+          }
+        }
+      }
+      st[gi].reset();
+    }
+    piece = 0;
+  };
+
+  // One 32-position half h of the staged stage for the first NG groups of
+  // this wave (NG is 2, or 1 when the unit has no tokens for the second):
+  // straight-line code, no branch between the transposed reads and the
+  // matrix-core instructions that use them.
+  auto half = [&](auto ng, int h, int ok, int stage0) {
+    constexpr int NG = decltype(ng)::value;
+    // K operands of the two 16-row blocks: row 16 b + col, chunk 4 kk + grp
+    uint4 ka[4], kb[4];
+    const PKV_LDS char* kbase = (const PKV_LDS char*)s_k + (32 * h + col) * kKRow + grp * 16;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      ka[kk] = __builtin_bit_cast(uint4, *(const PKV_LDS u32x4v*)(kbase + kk * 64));
+      kb[kk] = __builtin_bit_cast(uint4, *(const PKV_LDS u32x4v*)(kbase + 16 * kKRow + kk * 64));
+    }
+    const bool va = (ok >> (2 * h)) & 1;
+    const bool vb = (ok >> (2 * h + 1)) & 1;
+    uint4 p_hi[NG], p_lo[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const f32x4 Sa = Attend<T>::scores(ka, q[gi]);
+      const f32x4 Sb = Attend<T>::scores(kb, q[gi]);
+      // this column sees positions < lim of the half (relative to its start)
+      const int lim = live(cur, gi) ? cur.ctx - cur.qn + token_of(cur, gi) + 1 - stage0 - 32 * h
+                                    : 0;
+      float s8[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s8[i] = (va && 4 * grp + i < lim) ? Sa[i] * qk_scale : -INFINITY;
+        s8[4 + i] = (vb && 16 + 4 * grp + i < lim) ? Sb[i] * qk_scale : -INFINITY;
+      }
+      float mt = s8[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mt = fmaxf(mt, s8[i]);
+      mt = max_xor32(max_xor16(mt));
+      const float m_old = st[gi].m_run;
+      const float m_new = fmaxf(m_old, mt);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_old - m_use);
+      st[gi].m_run = m_new;
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(s8[i] - m_use);
+      st[gi].l_part = st[gi].l_part * alpha +
+                      (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+      split_p8<T>(p, p_hi[gi], p_lo[gi]);
+      // rescale only when some column's running max moved; a column with
+      // no max yet has nothing accumulated
+      if (__any(m_old != -INFINITY && alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) st[gi].acc[db] *= alpha;
+      }
+    }
+    // V^T operands of the 8 dim blocks: lane (d = col, group j) takes
+    // positions 4j..4j+3 of each 16-row block (the same k order as P);
+    // shared by the groups
+    const PKV_LDS char* vbase = (const PKV_LDS char*)s_v +
+                                (32 * h + 4 * grp + (col >> 2)) * kSlotRow + (col & 3) * 8;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (PKV_LDS s16x4*)(vbase + 32 * db));
+      const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (PKV_LDS s16x4*)(vbase + 16 * kSlotRow + 32 * db));
+      const uint2 u0 = __builtin_bit_cast(uint2, t0);
+      const uint2 u1 = __builtin_bit_cast(uint2, t1);
+      const uint4 vt = make_uint4(u0.x, u0.y, u1.x, u1.y);
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        st[gi].acc[db] = mfma_k32<T>(vt, p_hi[gi], st[gi].acc[db]);
+        st[gi].acc[db] = mfma_k32<T>(vt, p_lo[gi], st[gi].acc[db]);
+      }
+    }
+  };
+
+  // 3. the range, one stage at a time: barrier (every wave is done with the
+  //    LDS stage), stage i from registers into LDS (V rows past what the unit
+  //    sees are zeroed: P is 0 there and 0 * NaN would still be NaN), the
+  //    loads of stage i + 1 into the freed registers (in flight during this
+  //    stage's math), barrier, the math.
+  uint4 kr[kSub], vr[kSub];
+  load_q_unit(cur);
+  wait_all_loads();
+  int okb = load_stage(cur, kr, vr);
+  for (int i = 0; i < len; ++i) {
+    __syncthreads();
+    {
+      const int vl = vlimit(cur);
+#pragma unroll
+      for (int m = 0; m < kSub; ++m) {
+        const int row = ld_row + m * kTile;
+        uint4 v = vr[m];
+        if (row >= vl || !((okb >> m) & 1)) v = make_uint4(0, 0, 0, 0);
+        *(PKV_LDS u32x4v*)((PKV_LDS char*)s_k + row * kKRow + ld_chunk * 16) =
+            __builtin_bit_cast(u32x4v, kr[m]);
+        *(PKV_LDS u32x4v*)((PKV_LDS char*)s_v + row * kSlotRow + ld_chunk * 16) =
+            __builtin_bit_cast(u32x4v, v);
+      }
+    }
+    const int ok_now = okb;
+    const bool more = i + 1 < len;
+    PfCursor nx = cur;
+    if (more) {
+      nx = advance(cur);
+      okb = load_stage(nx, kr, vr);
+    }
+    __syncthreads();
+    const int stage0 = cur.t * kStage;
+    // groups are filled in order: the second has tokens only if the first does
+    if (group_live(cur, 1)) {
+      half(std::integral_constant<int, 2>(), 0, ok_now, stage0);
+      half(std::integral_constant<int, 2>(), 1, ok_now, stage0);
+    } else if (group_live(cur, 0)) {
+      half(std::integral_constant<int, 1>(), 0, ok_now, stage0);
+      half(std::integral_constant<int, 1>(), 1, ok_now, stage0);
+    }
+    const bool unit_ends = cur.t + 1 >= cur.n;
+    if (unit_ends || !more) finish(cur);
+    if (more && unit_ends) {
+      load_q_unit(nx);
+      // once per unit: the q loads are waited for here, with the next
+      // stage's (so no later wait has to count them)
+      wait_all_loads();
+    }
+    cur = nx;
+  }
+}
+
+// Resident workgroups per CU, per device and LDS size class, computed once.
+constexpr int kPfMaxDevices = 64;
+constexpr int kPfLdsClasses = 4;
+inline int pf_lds_class(size_t dyn) {
+  return dyn <= 2048 ? 0 : dyn <= 8192 ? 1 : dyn <= 16384 ? 2 : 3;
+}
+inline size_t pf_lds_class_bytes(int c) {
+  const size_t b[kPfLdsClasses] = {2048, 8192, 16384, (kMaxSeqsPrefill + 1) * sizeof(int)};
+  return b[c];
+}
+
+template <typename T>
+hipError_t prefill_grid(int& cus, int& per_cu, size_t dyn) {
+  static std::atomic<int> cache[kPfMaxDevices][kPfLdsClasses][2];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const int c = pf_lds_class(dyn);
+  if (dev >= 0 && dev < kPfMaxDevices) {
+    cus = cache[dev][c][0].load(std::memory_order_relaxed);
+    per_cu = cache[dev][c][1].load(std::memory_order_relaxed);
+    if (cus > 0 && per_cu > 0) return hipSuccess;
+  }
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_split_kernel<T>,
+                                                     kPfThreads, pf_lds_class_bytes(c));
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) per_cu = 1;
+  if (dev >= 0 && dev < kPfMaxDevices) {
+    cache[dev][c][1].store(per_cu, std::memory_order_relaxed);
+    cache[dev][c][0].store(cus, std::memory_order_relaxed);
+  }
+  return hipSuccess;
+}
+
+template <typename T>
+hipError_t launch_prefill_t(const DecodeArgs& a, hipStream_t stream) {
+  const size_t dyn = static_cast<size_t>(a.num_seqs + 1) * sizeof(int);
+  int cus = 0, per_cu = 0;
+  hipError_t e = prefill_grid<T>(cus, per_cu, dyn);
+  if (e != hipSuccess) return e;
+  int64_t per_kv = static_cast<int64_t>(cus) * per_cu / a.num_kv_heads;
+  if (per_kv < 1) per_kv = 1;
+  const int64_t wgs = per_kv * a.num_kv_heads;
+  prefill_split_kernel<T><<<dim3(static_cast<unsigned>(wgs)), dim3(kPfThreads), dyn, stream>>>(
+      a, static_cast<int>(per_kv));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_fast(const DecodeArgs& a, hipStream_t stream) {
+  return a.dtype == 2 ? launch_prefill_t<bf16_t>(a, stream) : launch_prefill_t<f16_t>(a, stream);
+}
+
+}  // namespace pkv

@@ -31,13 +31,14 @@ def say(*a):
     print(*a, flush=True)
 
 
-def _mix(name, dtype, hq, hkv, d, b, seed, n=12, hmax=300):
+def _mix(name, dtype, hq, hkv, d, b, seed, n=12, hmax=300, kinds=None):
     """Histories U{0..hmax}; query lengths cycle through the regimes: 0, 1
     (decode), 2..5 (speculative), a ragged chunk, a fresh prefill (no
-    history), and a chunk that spans several tiles and blocks."""
+    history), and chunks that span several tiles and blocks (long enough,
+    at G >= 3, for the prefill kernel: >= 128 (token, head) columns)."""
     rng = np.random.default_rng(seed)
     hist = rng.integers(0, hmax, size=n, endpoint=True)
-    kinds = [0, 1, 3, 4, 5, 17, 40, 1, 2, 33, 64, 1]
+    kinds = kinds or [0, 1, 3, 4, 5, 17, 40, 1, 2, 33, 64, 1]
     q = np.array([kinds[i % len(kinds)] for i in range(n)], np.int64)
     hist[4] = 0          # a fresh prefill: the chunk is the whole context
     hist[0] = max(hist[0], 1)   # a sequence with history but no query rows
@@ -52,6 +53,9 @@ SMALL = {
     "bf16_g3_b16": lambda: _mix("bf16_g3_b16", "bf16", 12, 4, 128, 16, 205),
     "f32_d8_b4": lambda: _mix("f32_d8_b4", "f32", 4, 2, 8, 4, 206, hmax=40),
     "bf16_d64_b8": lambda: _mix("bf16_d64_b8", "bf16", 8, 2, 64, 8, 207, hmax=100),
+    # MHA: chunks of 128+ tokens reach the prefill kernel (one head per KV head)
+    "f16_mha_long": lambda: _mix("f16_mha_long", "f16", 4, 4, 128, 16, 208, n=6,
+                                 kinds=[1, 130, 4, 200, 127, 257]),
 }
 
 
