@@ -92,6 +92,7 @@ def default_partition(workload):
 
 VARLEN = ("spec_verify_bf16", "mixed_prefill_bf16")
 BLOCK_MOVES = ("cow_fork_bf16", "swap_bf16")
+HOST_ONLY = ("prefix_cache",)
 PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
 
 
@@ -111,6 +112,74 @@ def _events_ms(fn, reps, flush=None):
         torch.cuda.synchronize()
         xs.append(e0.elapsed_time(e1))
     return float(np.mean(xs)), float(np.percentile(xs, 10)), float(np.percentile(xs, 90))
+
+
+def bench_prefix_cache(args):
+    """Host-only: admissions through the library's cached block pool (hash
+    the full blocks, longest cached prefix, touch, fresh blocks, cache the
+    new full blocks) for 512 requests, cold and then warm after releasing
+    them all; the oracle's pool timed on the same requests."""
+    import paged_kv_cache_113_amd as pkv
+    import workloads as W
+    reqs = W.prefix_requests()
+    B = 16
+    need = sum(-(-len(t) // B) for t in reqs)
+    n_blocks = int(math.ceil(1.1 * need))
+    toks_total = int(sum(len(t) for t in reqs))
+    blocks_full = int(sum(len(t) // B for t in reqs))
+
+    def run(make_pool, admit, cache, release):
+        pool = make_pool()
+        times, hits = [], []
+        for phase in range(2):
+            tables = []
+            t0 = time.perf_counter()
+            cached = 0
+            for t in reqs:
+                table, c = admit(pool, t)
+                cache(pool, table, t)
+                tables.append(table)
+                cached += c
+            times.append(time.perf_counter() - t0)
+            hits.append(cached)
+            for table in tables:
+                release(pool, table)
+        return times, hits
+
+    lib_t, lib_h = run(lambda: pkv.BlockPool(n_blocks, B),
+                       lambda p, t: p.admit(t), lambda p, tb, t: p.cache_full_blocks(tb, t),
+                       lambda p, tb: p.release(tb))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.prefix_cache as OP
+        ora_t, ora_h = run(lambda: OP.CachedBlockPool(n_blocks, B),
+                           lambda p, t: p.admit(t.tolist()),
+                           lambda p, tb, t: p.cache_full_blocks(tb, t.tolist()),
+                           lambda p, tb: p.release(tb))
+        assert ora_h == lib_h, (ora_h, lib_h)
+        cpu = {"value": round(toks_total * 2 / sum(ora_t), 1), "unit": "tokens/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"the same 512 requests, cold then warm, {sum(ora_t):.1f} s "
+                         "(hashlib SHA-256, Python pool)"}
+    # each block hashes a 96-byte message (parent hash + 16 int32 tokens) in
+    # two 64-byte compression blocks, on both admission and caching
+    value = toks_total * 2 / sum(lib_t)
+    line = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 0,
+            "steps": 2, "warmup": 0, "ms_per_step": round(sum(lib_t) / 2 * 1e3, 3),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+            "data": "synthetic",
+            "config": {"workload": "prefix_cache", "requests": len(reqs), "block_size": B,
+                       "pool_blocks": n_blocks, "tokens": toks_total, "full_blocks": blocks_full,
+                       "shared_prompt_tokens": 512},
+            "phases_ms": {"cold": round(lib_t[0] * 1e3, 3), "warm": round(lib_t[1] * 1e3, 3)},
+            "cached_tokens": {"cold": lib_h[0], "warm": lib_h[1]},
+            "blocks_hashed_per_s": round(blocks_full * 4 / sum(lib_t), 1),
+            "roofline": {"bound": "host", "achieved": round(value, 1), "peak": None,
+                         "unit": "tokens/s", "frac": None, "traffic": None,
+                         "kernel": "pkv_pool_admit + pkv_pool_cache_full_blocks (one host thread,"
+                                   " Python call overhead included)"},
+            "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
 
 
 def bench_block_moves(args):
@@ -315,7 +384,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode_step_bf16",
                     choices=["decode_step_bf16", "mha_fp16", "gqa_shared_bf16",
-                             "long_split_bf16", *VARLEN, *BLOCK_MOVES])
+                             "long_split_bf16", *VARLEN, *BLOCK_MOVES, *HOST_ONLY])
     ap.add_argument("--max-partitions", type=int, default=8,
                     help="multi-token workloads: pieces per query row at most")
     ap.add_argument("--partition-size", type=int, default=None)
@@ -338,6 +407,9 @@ def main():
 
     if args.workload in BLOCK_MOVES:
         bench_block_moves(args)
+        return
+    if args.workload in HOST_ONLY:
+        bench_prefix_cache(args)
         return
 
     import torch

@@ -63,7 +63,9 @@ enum pkv_status {
   PKV_ERR_UNSUPPORTED = -4, /* valid, but no kernel handles this shape */
   PKV_ERR_WORKSPACE = -5,   /* split requested without its workspace */
   PKV_ERR_LAUNCH = -6,      /* the HIP runtime refused a launch */
-  PKV_ERR_HOST = -7         /* a host buffer is too small or not pinned memory */
+  PKV_ERR_HOST = -7,        /* a host buffer is too small or not pinned memory */
+  PKV_ERR_STATE = -8,       /* not valid in the block pool's current state */
+  PKV_ERR_CAPACITY = -9     /* not enough free blocks (nothing was taken) */
 };
 
 /*
@@ -315,6 +317,96 @@ int paged_kv_swap_in(const void* host_src, int64_t host_bytes, void* const* k_ca
                      void* const* v_caches, int num_layers, const int64_t* block_ids,
                      int64_t num_ids, int64_t num_blocks, int num_kv_heads, int block_size,
                      int head_size, int dtype, void* stream);
+
+/*
+ * Prefix caching (host side, no GPU work): block identity and a block pool
+ * whose freed blocks stay hit-able until their slot is needed again.
+ *
+ * A full block's identity is SHA-256 over its token ids and extra keys, 32
+ * bytes ("vLLM source walkthrough: PagedAttention and continuous batching",
+ * section 1.9). So that an identity covers the whole prefix (equal tokens
+ * after different prefixes are different K/V), each block's message starts
+ * with the previous block's hash (32 zero bytes before the first block),
+ * then the block's tokens as little-endian int32, then the extra keys (for
+ * instance an adapter name or a cache salt).
+ *
+ * The pool follows the block life cycle of "vLLM PagedAttention: from
+ * fragmentation to slot mapping" (block metadata under prefix caching): each
+ * block has a reference count and an optional identity; free blocks wait in
+ * a FIFO queue (taken from the head, returned to the tail; an intrusive
+ * doubly linked list, O(1) unlinking); a ref-0 block with an identity stays
+ * hit-able in the queue; a hit takes it out of the queue ("touch") and
+ * counts a reference; taking a block for new data erases its identity;
+ * releasing a block to 0 returns it to the tail with its identity. A pool is
+ * host memory owned by its handle (pkv_pool_create / pkv_pool_destroy), not
+ * thread-safe (one caller at a time), and touches no device memory.
+ */
+typedef struct pkv_block_pool pkv_block_pool;
+
+/* pkv_block_hashes -- out[32 * b ..] = identity of full block b of tokens
+ * (block_size tokens each; a trailing partial block has none). Returns the
+ * number of full blocks (>= 0) or a negative pkv_status (PKV_ERR_NULL,
+ * PKV_ERR_SHAPE). Host pointers. */
+int64_t pkv_block_hashes(uint8_t* out, const int32_t* tokens, int64_t num_tokens, int block_size,
+                         const uint8_t* extra, int64_t extra_len);
+
+/* pkv_pool_create -- a pool of blocks 0..num_blocks-1, all free, queued in
+ * the order initial_free gives (a permutation of 0..num_blocks-1) or 0, 1,
+ * ... when it is NULL. *out receives the handle. Errors: PKV_ERR_NULL,
+ * PKV_ERR_SHAPE (sizes < 1, not a permutation), PKV_ERR_STATE (out of host
+ * memory). */
+int pkv_pool_create(pkv_block_pool** out, int num_blocks, int block_size,
+                    const int32_t* initial_free);
+/* pkv_pool_destroy -- frees the pool (NULL is ignored). */
+void pkv_pool_destroy(pkv_block_pool* pool);
+/* pkv_pool_num_free -- blocks in the free queue (cached or not). */
+int64_t pkv_pool_num_free(const pkv_block_pool* pool);
+
+/* pkv_pool_longest_hit -- the blocks of the leading hashes[32 * i ..] that
+ * are cached, up to the first miss, into out_blocks; returns how many.
+ * Changes nothing. */
+int pkv_pool_longest_hit(const pkv_block_pool* pool, const uint8_t* hashes, int num_hashes,
+                         int32_t* out_blocks);
+/* pkv_pool_touch -- one more reference on each listed block; a ref-0 block
+ * leaves the free queue (a hit on a cached-free block). Errors:
+ * PKV_ERR_SHAPE (an id outside the pool; nothing changed). */
+int pkv_pool_touch(pkv_block_pool* pool, const int32_t* blocks, int n);
+/* pkv_pool_allocate -- n blocks from the head of the free queue for new
+ * data (reference count 1, identity erased). PKV_ERR_CAPACITY when fewer
+ * than n are free; nothing is taken then. */
+int pkv_pool_allocate(pkv_block_pool* pool, int n, int32_t* out_blocks);
+/* pkv_pool_cache -- give an in-use full block the identity hash[0..31].
+ * Returns 1 when cached, 0 when the block already has an identity or the
+ * hash already names a block (the first keeps it), PKV_ERR_STATE for a
+ * block not in use, PKV_ERR_SHAPE for an id outside the pool. */
+int pkv_pool_cache(pkv_block_pool* pool, int32_t block, const uint8_t* hash);
+/* pkv_pool_release -- one reference less on each listed block, in order; a
+ * block at 0 goes to the tail of the free queue and keeps its identity.
+ * PKV_ERR_STATE when a block is listed more often than it is referenced;
+ * nothing changes then. */
+int pkv_pool_release(pkv_block_pool* pool, const int32_t* blocks, int n);
+
+/* pkv_pool_admit -- blocks for a request of num_tokens tokens: its longest
+ * run of leading cached blocks, capped at (num_tokens - 1) / block_size
+ * blocks so that the last token is recomputed (walkthrough page, section
+ * 1.9), by reference (touched), and fresh blocks for the rest.
+ * out_table receives ceil(num_tokens / block_size) block ids and
+ * *cached_tokens the tokens the hit covers. PKV_ERR_CAPACITY (nothing
+ * changed) when the free blocks do not suffice. */
+int pkv_pool_admit(pkv_block_pool* pool, const int32_t* tokens, int64_t num_tokens,
+                   const uint8_t* extra, int64_t extra_len, int32_t* out_table,
+                   int64_t* cached_tokens);
+/* pkv_pool_cache_full_blocks -- after a request's K/V are written, its full
+ * blocks (table[0 .. num_tokens / block_size - 1]) get their identities
+ * (blocks that have one, and hashes already taken, are left as they are). */
+int pkv_pool_cache_full_blocks(pkv_block_pool* pool, const int32_t* table,
+                               const int32_t* tokens, int64_t num_tokens, const uint8_t* extra,
+                               int64_t extra_len);
+/* pkv_pool_state -- for checks: reference counts [num_blocks], the free
+ * queue from head to tail, and a cached flag per block (each may be NULL).
+ * Returns the number of free blocks. */
+int pkv_pool_state(const pkv_block_pool* pool, int32_t* ref_out, int32_t* free_out,
+                   uint8_t* cached_out);
 
 /* pkv_strerror -- static description of a pkv_status code. */
 const char* pkv_strerror(int code);

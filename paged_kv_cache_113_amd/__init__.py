@@ -39,6 +39,18 @@ SIGNATURES = {
     "paged_attention_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "paged_kv_gather": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32,
                                _I32, _I32, _P]),
+    "pkv_block_hashes": (_I64, [_P, _P, _I64, _I32, _P, _I64]),
+    "pkv_pool_create": (_I32, [_P, _I32, _I32, _P]),
+    "pkv_pool_destroy": (None, [_P]),
+    "pkv_pool_num_free": (_I64, [_P]),
+    "pkv_pool_longest_hit": (_I32, [_P, _P, _I32, _P]),
+    "pkv_pool_touch": (_I32, [_P, _P, _I32]),
+    "pkv_pool_allocate": (_I32, [_P, _I32, _P]),
+    "pkv_pool_cache": (_I32, [_P, _I32, _P]),
+    "pkv_pool_release": (_I32, [_P, _P, _I32]),
+    "pkv_pool_admit": (_I32, [_P, _P, _I64, _P, _I64, _P, _P]),
+    "pkv_pool_cache_full_blocks": (_I32, [_P, _P, _P, _I64, _P, _I64]),
+    "pkv_pool_state": (_I32, [_P, _P, _P, _P]),
     "pkv_strerror": (ctypes.c_char_p, [_I32]),
 }
 
@@ -239,6 +251,108 @@ def paged_kv_gather(k_out, v_out, k_cache, v_cache, block_table, context_lens, s
         _ptr(k_out), _ptr(v_out), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(context_lens), s, hkv, d, b, n, block_table.shape[1], max_ctx,
         _DTYPE[k_cache.dtype], _stream(stream)))
+
+
+# -- prefix caching (host side) ---------------------------------------------------
+
+def _host_i32(x):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _bytes_ptr(b):
+    if not b:
+        return None, 0
+    buf = ctypes.create_string_buffer(bytes(b), len(b))
+    return buf, len(b)
+
+
+def block_hashes(tokens, block_size, extra=b""):
+    """32-byte identities of the full blocks of ``tokens`` (a list of bytes)."""
+    a, ap = _host_i32(tokens)
+    nb = len(a) // block_size
+    out = ctypes.create_string_buffer(max(1, 32 * nb))
+    eb, el = _bytes_ptr(extra)
+    n = lib.pkv_block_hashes(out, ap, len(a), block_size, eb, el)
+    _check("pkv_block_hashes", n if n < 0 else 0)
+    raw = out.raw
+    return [raw[32 * i:32 * i + 32] for i in range(n)]
+
+
+class BlockPool:
+    """The library's cached block pool (host memory, one caller at a time)."""
+
+    def __init__(self, num_blocks, block_size, initial_free=None):
+        self.num_blocks, self.block_size = num_blocks, block_size
+        h = ctypes.c_void_p()
+        if initial_free is None:
+            code = lib.pkv_pool_create(ctypes.byref(h), num_blocks, block_size, None)
+        else:
+            a, ap = _host_i32(initial_free)
+            code = lib.pkv_pool_create(ctypes.byref(h), num_blocks, block_size, ap)
+        _check("pkv_pool_create", code)
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib.pkv_pool_destroy(h)
+            self._h = None
+
+    def num_free(self):
+        return int(lib.pkv_pool_num_free(self._h))
+
+    def longest_hit(self, hashes):
+        buf = ctypes.create_string_buffer(b"".join(hashes), max(1, 32 * len(hashes)))
+        out = (ctypes.c_int32 * max(1, len(hashes)))()
+        k = lib.pkv_pool_longest_hit(self._h, buf, len(hashes), out)
+        _check("pkv_pool_longest_hit", k if k < 0 else 0)
+        return list(out[:k])
+
+    def touch(self, blocks):
+        a, ap = _host_i32(blocks)
+        _check("pkv_pool_touch", lib.pkv_pool_touch(self._h, ap, len(a)))
+
+    def allocate(self, n):
+        out = (ctypes.c_int32 * max(1, n))()
+        _check("pkv_pool_allocate", lib.pkv_pool_allocate(self._h, n, out))
+        return list(out[:n])
+
+    def cache(self, block, h):
+        code = lib.pkv_pool_cache(self._h, block, ctypes.create_string_buffer(bytes(h), 32))
+        _check("pkv_pool_cache", code if code < 0 else 0)
+        return bool(code)
+
+    def release(self, blocks):
+        a, ap = _host_i32(blocks)
+        _check("pkv_pool_release", lib.pkv_pool_release(self._h, ap, len(a)))
+
+    def admit(self, tokens, extra=b""):
+        a, ap = _host_i32(tokens)
+        nb = -(-len(a) // self.block_size)
+        out = (ctypes.c_int32 * max(1, nb))()
+        cached = ctypes.c_int64()
+        eb, el = _bytes_ptr(extra)
+        _check("pkv_pool_admit", lib.pkv_pool_admit(self._h, ap, len(a), eb, el, out,
+                                                    ctypes.byref(cached)))
+        return list(out[:nb]), int(cached.value)
+
+    def cache_full_blocks(self, table, tokens, extra=b""):
+        t, tp = _host_i32(table)
+        a, ap = _host_i32(tokens)
+        eb, el = _bytes_ptr(extra)
+        _check("pkv_pool_cache_full_blocks",
+               lib.pkv_pool_cache_full_blocks(self._h, tp, ap, len(a), eb, el))
+
+    def state(self):
+        """(reference counts, free queue head to tail, cached flags)."""
+        ref = (ctypes.c_int32 * self.num_blocks)()
+        free = (ctypes.c_int32 * self.num_blocks)()
+        cached = (ctypes.c_uint8 * self.num_blocks)()
+        n = lib.pkv_pool_state(self._h, ref, free, cached)
+        _check("pkv_pool_state", n if n < 0 else 0)
+        return list(ref), list(free[:n]), [bool(c) for c in cached]
 
 
 def pkv_strerror(code):

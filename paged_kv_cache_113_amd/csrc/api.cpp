@@ -297,6 +297,8 @@ const char* pkv_strerror(int code) {
     case PKV_ERR_WORKSPACE: return "split mode needs max_logits, exp_sums and tmp_out";
     case PKV_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case PKV_ERR_HOST: return "the host buffer is too small or not pinned memory the GPU reaches";
+    case PKV_ERR_STATE: return "not valid in the block pool's current state";
+    case PKV_ERR_CAPACITY: return "not enough free blocks (nothing was taken)";
     default: return "unknown pkv status code";
   }
 }

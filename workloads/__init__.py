@@ -348,6 +348,27 @@ def cow_fork_bf16(num_prompts: int = 128, branches: int = 4, lo: int = 64, hi: i
                  slots=np.array(slots, np.int64))
 
 
+def prefix_requests(num: int = 512, lo: int = 64, hi: int = 4096, shared: int = 512,
+                    share_frac: float = 0.3, vocab: int = 32000, seed: int = 1009):
+    """Token ids of ``num`` requests with U{lo..hi} tokens; round(share_frac
+    * num) of them (a seeded choice among those longer than the shared part)
+    start with the same ``shared``-token system prompt. Returns a list of
+    int32 arrays."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(lo, hi, size=num, endpoint=True)
+    system = rng.integers(0, vocab, size=shared).astype(np.int32)
+    eligible = np.flatnonzero(lens > shared)
+    k = min(len(eligible), int(round(share_frac * num)))
+    sharers = set(rng.permutation(eligible)[:k].tolist())
+    out = []
+    for i, n in enumerate(lens):
+        t = rng.integers(0, vocab, size=int(n)).astype(np.int32)
+        if i in sharers:
+            t[:shared] = system
+        out.append(t)
+    return out
+
+
 CASES = {
     "tiny": tiny_page_example,
     "mha_fp16": mha_fp16,
