@@ -44,7 +44,11 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode KV-read HBM GB/s (% of MI355X peak) + decoded seqs·tokens/s"
 HBM_PEAK_GBS = 8000.0
 DECODE_SOURCES = ["paged_kv_cache_113_amd/csrc/decode_fast.hip",
-                  "paged_kv_cache_113_amd/csrc/device.h"]
+                  "paged_kv_cache_113_amd/csrc/device.h",
+                  "paged_kv_cache_113_amd/csrc/mfma_tile.h",
+                  "paged_kv_cache_113_amd/csrc/varlen.h"]
+VARLEN_SOURCES = DECODE_SOURCES + ["paged_kv_cache_113_amd/csrc/prefill.hip",
+                                   "paged_kv_cache_113_amd/csrc/decode_generic.hip"]
 MOVE_SOURCES = ["paged_kv_cache_113_amd/csrc/block_ops.hip",
                 "paged_kv_cache_113_amd/csrc/device.h"]
 
@@ -558,7 +562,8 @@ def main():
     value = step_bytes / (ms_per_step / 1e3) / 1e9
     achieved = layer_bytes / (dec_ms / 1e3) / 1e9
     positions = float(np.sum(batch.context_lens, dtype=np.int64))
-    traffic = traffic_for(args.workload)
+    traffic = traffic_for(args.workload, "paged_varlen_attention", VARLEN_SOURCES) if varlen \
+        else traffic_for(args.workload)
     pairs = float(visible_pairs(batch).sum()) if varlen else positions
     flops = 4.0 * batch.num_heads * batch.head_size * pairs   # q.K and P.V, per layer
 
@@ -597,7 +602,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "paged_varlen_attention (split kernel + merge)" if varlen
+                     "kernel": "paged_varlen_attention (split kernel, prefill kernel, merge)"
+                     if varlen
                      else "decode_split_kernel" if P > 0 else "decode_whole_kernel",
                      "bytes_per_launch": layer_bytes,
                      "logical_bytes_per_launch": logical_bytes,

@@ -24,6 +24,15 @@ def test_block_hashes_match_oracle(pkv, seed):
     assert pkv.block_hashes(toks, B, extra) == oracle_hashes(toks, B, extra)
 
 
+def test_block_hashes_every_padding_boundary(pkv):
+    # message lengths 36 .. 165 bytes: every place the SHA-256 padding and
+    # length field can fall within one or two 64-byte compression blocks
+    toks = [7, -3, 2**31 - 1, -2**31]
+    for n in range(0, 130):
+        extra = bytes(range(n % 256))[:n]
+        assert pkv.block_hashes(toks[:1], 1, extra) == oracle_hashes(toks[:1], 1, extra), n
+
+
 def _same_state(lib_pool, ora):
     ref, free, cached = lib_pool.state()
     assert ref == ora.ref
