@@ -207,7 +207,9 @@ int paged_attention_reduce(float* out, const float* max_logits, const float* exp
  * max_logits/exp_sums [num_tokens, num_heads, max_partitions] and tmp_out
  * [num_tokens, num_heads, max_partitions, head_size] float32 (size:
  * paged_attention_workspace_bytes(num_tokens, ...)), and merges them. The
- * plain path (other shapes) ignores the workspace. Rows no sequence claims
+ * matrix-core path covers the shapes of paged_decode_attention's fast path
+ * with a finite scale > 0; the plain path (everything else) ignores the
+ * workspace. Rows no sequence claims
  * are undefined; rows past a sequence's context (q_s > ctx_s, a caller
  * error) get 0.
  *

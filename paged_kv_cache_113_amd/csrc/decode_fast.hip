@@ -635,6 +635,8 @@ bool fast_varlen_supported(const DecodeArgs& a) {
   if (!((a.dtype == 1 || a.dtype == 2) && a.head_size == kD && a.block_size % kTile == 0 &&
         G >= 1 && G <= 16 && a.num_seqs <= kMaxSeqsBalanced))
     return false;
+  // the prefill kernel takes its running max on unscaled scores
+  if (!(a.scale > 0.f && a.scale <= 3.0e38f)) return false;
   // the stream of (sequence, column group) tiles is indexed with 32 bits: a
   // sequence has at most q_s / tpg + 1 groups of at most ceil(cap / 16) tiles
   const int64_t groups = a.num_tokens / (kTile / G) + a.num_seqs;

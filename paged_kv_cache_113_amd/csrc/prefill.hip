@@ -55,6 +55,14 @@ constexpr int kMaxSeqsPrefill = 8192;                      // LDS prefix capacit
 constexpr int kXcdCount = 8;                               // MI355X: 8 XCDs
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// The running max a column's probabilities are taken against moves only when
+// a score exceeds it by more than this (log2 units): probabilities then stay
+// below 2^8, and the accumulators are rescaled only on such a move instead of
+// whenever the max creeps up. The partial (max, sum, output) stays exact: the
+// sum and the output are taken against the same reference.
+constexpr float kLazyLog2 = 8.f;
 
 // s_waitcnt vmcnt(0): every vector memory load issued so far has arrived.
 __device__ __forceinline__ void wait_all_loads() {
@@ -63,15 +71,34 @@ __device__ __forceinline__ void wait_all_loads() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// 8 probabilities in [0, 1] as 16-bit high parts and the 16-bit roundings of
-// the remainders, packed in k order (a 16x16x32 operand).
+// Two probabilities as their 16-bit roundings (high parts) and the 16-bit
+// roundings of the remainders, each pair packed in one register: hi + lo is
+// p to about 2^-16 relative (packed conversions, two values per instruction).
+template <typename T>
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const f32x2v x = {a, b};
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, h2));
+    // a bf16 value is the top half of the float with the same bits
+    const f32x2v hf = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(x - hf, h2));
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = __builtin_convertvector(x, h2);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t,
+                            __builtin_convertvector(x - __builtin_convertvector(h, f32x2v), h2));
+  }
+}
+
+// 8 probabilities in k order as a 16x16x32 operand pair (high parts, remainders).
 template <typename T>
 __device__ __forceinline__ void split_p8(const float* p, uint4& hi, uint4& lo) {
-  uint2 h0, l0, h1, l1;
-  split_p<T>(p, h0, l0);
-  split_p<T>(p + 4, h1, l1);
-  hi = make_uint4(h0.x, h0.y, h1.x, h1.y);
-  lo = make_uint4(l0.x, l0.y, l1.x, l1.y);
+  split_pair<T>(p[0], p[1], hi.x, lo.x);
+  split_pair<T>(p[2], p[3], hi.y, lo.y);
+  split_pair<T>(p[4], p[5], hi.z, lo.z);
+  split_pair<T>(p[6], p[7], hi.w, lo.w);
 }
 
 // A stage of the per-KV-head stream: stage t of the n stages of unit (s, u).
@@ -351,8 +378,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
   // One 32-position half h of the staged stage for the first NG groups of
   // this wave (NG is 2, or 1 when the unit has no tokens for the second):
   // straight-line code, no branch between the transposed reads and the
-  // matrix-core instructions that use them.
-  auto half = [&](auto ng, int h, int ok, int stage0) {
+  // matrix-core instructions that use them. masked (wave-uniform): the
+  // stage reaches past some column's causal limit or misses a block; without
+  // it every position of the stage is visible to every live column of the
+  // wave (dead columns, whose q is zero, compute finite values that are
+  // never written).
+  auto half = [&](auto ng, bool masked, int h, int ok, int stage0) {
     constexpr int NG = decltype(ng)::value;
     // K operands of the two 16-row blocks: row 16 b + col, chunk 4 kk + grp
     uint4 ka[4], kb[4];
@@ -362,40 +393,49 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
       ka[kk] = __builtin_bit_cast(uint4, *(const PKV_LDS u32x4v*)(kbase + kk * 64));
       kb[kk] = __builtin_bit_cast(uint4, *(const PKV_LDS u32x4v*)(kbase + 16 * kKRow + kk * 64));
     }
-    const bool va = (ok >> (2 * h)) & 1;
-    const bool vb = (ok >> (2 * h + 1)) & 1;
     uint4 p_hi[NG], p_lo[NG];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       const f32x4 Sa = Attend<T>::scores(ka, q[gi]);
       const f32x4 Sb = Attend<T>::scores(kb, q[gi]);
-      // this column sees positions < lim of the half (relative to its start)
-      const int lim = live(cur, gi) ? cur.ctx - cur.qn + token_of(cur, gi) + 1 - stage0 - 32 * h
-                                    : 0;
       float s8[8];
+      if (masked) {
+        const bool va = (ok >> (2 * h)) & 1;
+        const bool vb = (ok >> (2 * h + 1)) & 1;
+        // this column sees positions < lim of the half (relative to its start)
+        const int lim = live(cur, gi) ? cur.ctx - cur.qn + token_of(cur, gi) + 1 - stage0 - 32 * h
+                                      : 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s8[i] = (va && 4 * grp + i < lim) ? Sa[i] * qk_scale : -INFINITY;
-        s8[4 + i] = (vb && 16 + 4 * grp + i < lim) ? Sb[i] * qk_scale : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          s8[i] = (va && 4 * grp + i < lim) ? Sa[i] : -INFINITY;
+          s8[4 + i] = (vb && 16 + 4 * grp + i < lim) ? Sb[i] : -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s8[i] = Sa[i];
+          s8[4 + i] = Sb[i];
+        }
       }
-      float mt = s8[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mt = fmaxf(mt, s8[i]);
-      mt = max_xor32(max_xor16(mt));
+      // the max is taken on the raw scores: scaling by qk_scale > 0 keeps it
+      float mt = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])),
+                       fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
+      mt = max_xor32(max_xor16(mt)) * qk_scale;
       const float m_old = st[gi].m_run;
-      const float m_new = fmaxf(m_old, mt);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_old - m_use);
-      st[gi].m_run = m_new;
+      const bool move = mt > m_old + kLazyLog2;
+      const float m_ref = move ? mt : m_old;
+      st[gi].m_run = m_ref;
+      // a column with no visible position yet keeps -inf
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      const float alpha = move ? fast_exp2(m_old - m_use) : 1.f;
       float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(s8[i] - m_use);
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(s8[i], qk_scale, -m_use));
       st[gi].l_part = st[gi].l_part * alpha +
                       (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
       split_p8<T>(p, p_hi[gi], p_lo[gi]);
-      // rescale only when some column's running max moved; a column with
-      // no max yet has nothing accumulated
-      if (__any(m_old != -INFINITY && alpha != 1.f)) {
+      // a column with no max yet has nothing accumulated
+      if (__any(move && m_old != -INFINITY)) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) st[gi].acc[db] *= alpha;
       }
@@ -455,13 +495,20 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
     }
     __syncthreads();
     const int stage0 = cur.t * kStage;
+    // the whole stage is visible to the wave's first token (the others see
+    // more) and all its blocks are in the pool: no masking
+    const int first_tok = cur.u * utok + kGroupsPerWave * w * tpg;
+    const bool interior = ok_now == (1 << kSub) - 1 &&
+                          stage0 + kStage <= cur.ctx - cur.qn + first_tok + 1;
+    using Two = std::integral_constant<int, 2>;
+    using One = std::integral_constant<int, 1>;
     // groups are filled in order: the second has tokens only if the first does
     if (group_live(cur, 1)) {
-      half(std::integral_constant<int, 2>(), 0, ok_now, stage0);
-      half(std::integral_constant<int, 2>(), 1, ok_now, stage0);
+      half(Two(), !interior, 0, ok_now, stage0);
+      half(Two(), !interior, 1, ok_now, stage0);
     } else if (group_live(cur, 0)) {
-      half(std::integral_constant<int, 1>(), 0, ok_now, stage0);
-      half(std::integral_constant<int, 1>(), 1, ok_now, stage0);
+      half(One(), true, 0, ok_now, stage0);
+      half(One(), true, 1, ok_now, stage0);
     }
     const bool unit_ends = cur.t + 1 >= cur.n;
     if (unit_ends || !more) finish(cur);

@@ -85,7 +85,7 @@ def max_err(got, want):
     return float(np.abs(g - want).max()) if want.size else 0.0
 
 
-def gpu_varlen(pkv, batch, t, meta, dev, max_partitions=8):
+def gpu_varlen(pkv, batch, t, meta, dev, max_partitions=8, scale=None):
     """Multi-token attention through the C ABI; the workspace starts as NaN
     so that a slot the kernels forget shows up in the output."""
     T, H, D = batch.num_tokens, batch.num_heads, batch.head_size
@@ -96,17 +96,19 @@ def gpu_varlen(pkv, batch, t, meta, dev, max_partitions=8):
     to = torch.full(shape + (D,), float("nan"), device=dev)
     qsl = torch.as_tensor(batch.query_start_loc, device=dev)
     pkv.paged_varlen_attention(out, t["q"], t["k_cache"], t["v_cache"], meta["table"], qsl,
-                               meta["ctx"], scale_of(batch), max_partitions, ml, es, to)
+                               meta["ctx"], scale_of(batch) if scale is None else scale,
+                               max_partitions, ml, es, to)
     return out
 
 
-def oracle_varlen(batch, q, k, v, seqs=None):
+def oracle_varlen(batch, q, k, v, seqs=None, scale=None):
     """The oracle's multi-token attention on the host copies; with ``seqs``,
     on those sequences only (returns their rows, in order)."""
     qsl = batch.query_start_loc
     if seqs is None:
         return oracle.attention_varlen(q, k, v, batch.block_table, qsl, batch.context_lens,
-                                       scale_of(batch), batch.dtype, threads=THREADS)
+                                       scale_of(batch) if scale is None else scale,
+                                       batch.dtype, threads=THREADS)
     rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs]).astype(np.int64)
     sub_q = q[torch.as_tensor(rows)]
     ql = np.array([qsl[s + 1] - qsl[s] for s in seqs], np.int64)

@@ -76,6 +76,53 @@ def test_varlen_small(dev, pkv, name):
         assert e <= TOL, (name, mp, e)
 
 
+def test_varlen_growing_scores(dev, pkv):
+    """K rows at position t scaled by 0.02 t: the scores' spread grows along
+    the context, so a column's running max climbs many times, often by far
+    more than the prefill kernel lets its reference max lag (and stays
+    within it at other times), inside one piece and across pieces."""
+    b = _mix("bf16_ramp", "bf16", 16, 4, 128, 16, 209, n=6, hmax=700,
+             kinds=[96, 1, 40, 130, 64, 1])
+    say(f"case: varlen growing scores q={b.query_lens.tolist()} ctx={b.context_lens.tolist()}")
+    t = W.layer_tensors(b, device=dev)
+    blk, off, fac = [], [], []
+    for s in range(b.num_seqs):
+        for p in range(int(b.context_lens[s])):
+            blk.append(int(b.block_table[s][p // b.block_size]))
+            off.append(p % b.block_size)
+            fac.append(0.02 * p)
+    blk = torch.as_tensor(blk, device=dev)
+    off = torch.as_tensor(off, device=dev)
+    fac = torch.as_tensor(fac, device=dev, dtype=torch.float32)
+    kc = t["k_cache"]
+    kc[blk, :, off, :] = (kc[blk, :, off, :].float() * fac[:, None, None]).to(kc.dtype)
+    meta = device_meta(b, dev)
+    th = host(t)
+    want = oracle_varlen(b, th["q"], th["k_cache"], th["v_cache"])
+    for mp in (1, 8):
+        got = gpu_varlen(pkv, b, t, meta, dev, mp)
+        torch.cuda.synchronize()
+        e = max_err(got.cpu(), want)
+        say(f"  max_partitions={mp}: max abs err {e:.3e}")
+        assert e <= TOL, (mp, e)
+
+
+def test_varlen_nonpositive_scale(dev, pkv):
+    """A negative or zero scale is valid (softmax of the negated or of equal
+    scores); the call routes it to the plain kernel."""
+    b = SMALL["bf16_g4_b16"]()
+    t = W.layer_tensors(b, device=dev)
+    meta = device_meta(b, dev)
+    th = host(t)
+    for scale in (-0.0883883, 0.0):
+        want = oracle_varlen(b, th["q"], th["k_cache"], th["v_cache"], scale=scale)
+        got = gpu_varlen(pkv, b, t, meta, dev, 8, scale=scale)
+        torch.cuda.synchronize()
+        e = max_err(got.cpu(), want)
+        say(f"case: varlen scale {scale}: max abs err {e:.3e}")
+        assert e <= TOL, (scale, e)
+
+
 def test_varlen_one_token_each_matches_decode(dev, pkv):
     """q_s = 1 everywhere: the same answer as decode attention (both within
     the bar of the oracle, and close to each other)."""
