@@ -154,82 +154,132 @@ __global__ __launch_bounds__(64) void varlen_generic_kernel(DecodeArgs a) {
   st.store(a.out + unit * D, D, lane);
 }
 
-// Merge of split partials: one wave per (sequence, head), four per
-// workgroup, no LDS and no barrier. Every slot with l_p > 0 takes part (a
-// real partial has l_p >= 1: its largest score contributes e^0); unused
-// slots carry l_p = 0. Lanes read the slots' (m, l) 64 at a time; a ballot
-// gives the used ones, whose weights w_p = l_p e^{m_p - M} are broadcast with
-// readlane while every lane accumulates its dims (d = lane + 64k) of o_p.
+// Merge of split partials: 16 lanes per (row, head) unit, four units per
+// wave, four waves per workgroup, no LDS and no barrier. Every slot with
+// l_p > 0 takes part (a real partial has l_p > 0); unused slots carry l_p = 0
+// and their output rows are never read. A unit's lanes read its slots'
+// (m, l) 16 at a time; a ballot gives the used ones, whose weights
+// w_p = l_p e^{m_p - M} are broadcast inside the unit while its lanes
+// accumulate their dims of o_p, four slots in flight per round. kVec: the
+// head size is a multiple of 64 and each lane moves 16 B per 64 dims (dims
+// 4j .. 4j + 3 + 64k); otherwise one float per 16 dims (dims j + 16k).
 constexpr int kRedWaves = 4;
+constexpr int kRedUnits = 4;    // units per wave
+constexpr int kRedLanes = 16;   // lanes per unit
+constexpr int kRedSlots = 4;    // slots in flight per round
 
+__device__ __forceinline__ float unit_max(float v) {
+#pragma unroll
+  for (int off = kRedLanes / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kRedLanes));
+  return v;
+}
+__device__ __forceinline__ float unit_sum(float v) {
+#pragma unroll
+  for (int off = kRedLanes / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kRedLanes);
+  return v;
+}
+
+template <bool kVec>
 __global__ __launch_bounds__(kRedWaves * 64) void reduce_kernel(
     float* __restrict__ out, const float* __restrict__ max_logits,
     const float* __restrict__ exp_sums, const float* __restrict__ tmp_out,
     const int32_t* __restrict__ context_lens, int num_seqs, int num_heads, int head_size,
     int max_partitions) {
+  // per lane: kVec 4 float4 (D <= 256), else 16 floats (D <= 256)
+  constexpr int kPer = 16;
   const int lane = threadIdx.x & 63;
-  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kRedWaves +
-                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (unit >= static_cast<int64_t>(num_seqs) * num_heads) return;
-  const int seq = static_cast<int>(unit / num_heads);
+  const int sub = lane >> 4;
+  const int j = lane & (kRedLanes - 1);
+  const int64_t total = static_cast<int64_t>(num_seqs) * num_heads;
+  const int64_t first = (static_cast<int64_t>(blockIdx.x) * kRedWaves +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kRedUnits;
+  if (first >= total) return;  // the whole wave
+  const int64_t unit = first + sub;
+  const bool active = unit < total;
+  const int64_t orow = active ? unit : first;  // = seq * num_heads + h
+  const int seq = static_cast<int>(orow / num_heads);
   const int D = head_size;
-  const int64_t orow = unit;  // = seq * num_heads + h
+  const int mp = max_partitions;
   // without lengths every row takes part (multi-token queries: every query
   // row's pieces are written, unused ones with l = 0)
-  const int n = (context_lens == nullptr || read_only(context_lens + seq) > 0) ? max_partitions : 0;
-  const float* __restrict__ m = max_logits + orow * max_partitions;
-  const float* __restrict__ l = exp_sums + orow * max_partitions;
-  const float* __restrict__ o = tmp_out + orow * max_partitions * D;
+  const int n = !active ? 0
+                : (context_lens == nullptr || read_only(context_lens + seq) > 0) ? mp : 0;
+  const float* __restrict__ m = max_logits + orow * mp;
+  const float* __restrict__ l = exp_sums + orow * mp;
+  const float* __restrict__ o = tmp_out + orow * mp * D;
 
   float mx = -INFINITY;
-  for (int p = lane; p < n; p += 64)
+  for (int p = j; p < n; p += kRedLanes)
     if (l[p] > 0.f) mx = fmaxf(mx, m[p]);
-  const float M = wave_max(mx);
+  const float M = unit_max(mx);
 
-  float acc[kMaxPerLane] = {0.f, 0.f, 0.f, 0.f};
+  float acc[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
   float den = 0.f;
-  for (int c0 = 0; c0 < n; c0 += 64) {
-    const int p = c0 + lane;
+  for (int c0 = 0; c0 < mp; c0 += kRedLanes) {  // uniform over the wave
+    const int p = c0 + j;
     float wp = 0.f;
     if (p < n) {
       const float lp = l[p];
       wp = lp > 0.f ? lp * expf(m[p] - M) : 0.f;
     }
     den += wp;
-    uint64_t used = __ballot(wp != 0.f);
-    // four used slots per round, so four rows are in flight at once
-    while (used) {
-      int b[4];
-      float wb[4];
+    uint32_t used = static_cast<uint32_t>(__ballot(wp != 0.f) >> (kRedLanes * sub)) & 0xffffu;
+    while (__any(used != 0u)) {
+      int b[kRedSlots];
+      float wb[kRedSlots];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        b[u] = used ? __builtin_ctzll(used) : -1;
-        used &= used ? used - 1 : 0;
-        wb[u] = b[u] < 0 ? 0.f
-                         : __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                         __builtin_bit_cast(int, wp), b[u]));
+      for (int u = 0; u < kRedSlots; ++u) {
+        b[u] = used ? __builtin_ctz(used) : -1;
+        used &= used ? used - 1u : 0u;
+        wb[u] = __shfl(wp, kRedLanes * sub + (b[u] < 0 ? 0 : b[u]), 64);
       }
-      float v[4][kMaxPerLane];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kRedSlots; ++u) {
         const float* __restrict__ row = o + static_cast<int64_t>(c0 + (b[u] < 0 ? 0 : b[u])) * D;
+        if constexpr (kVec) {
 #pragma unroll
-        for (int k = 0; k < kMaxPerLane; ++k) {
-          const int d = lane + 64 * k;
-          v[u][k] = (b[u] >= 0 && d < D) ? row[d] : 0.f;
+          for (int k = 0; k < kPer / 4; ++k) {
+            const int d = 4 * j + 64 * k;
+            if (b[u] >= 0 && d < D) {
+              const float4 v = *reinterpret_cast<const float4*>(row + d);
+              acc[4 * k + 0] = fmaf(wb[u], v.x, acc[4 * k + 0]);
+              acc[4 * k + 1] = fmaf(wb[u], v.y, acc[4 * k + 1]);
+              acc[4 * k + 2] = fmaf(wb[u], v.z, acc[4 * k + 2]);
+              acc[4 * k + 3] = fmaf(wb[u], v.w, acc[4 * k + 3]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < kPer; ++k) {
+            const int d = j + kRedLanes * k;
+            if (b[u] >= 0 && d < D) acc[k] = fmaf(wb[u], row[d], acc[k]);
+          }
         }
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int k = 0; k < kMaxPerLane; ++k) acc[k] = fmaf(wb[u], v[u][k], acc[k]);
     }
   }
-  den = wave_sum(den);
+  den = unit_sum(den);
+  if (!active) return;
+  const bool any = n > 0 && den > 0.f;
+  float* __restrict__ dst = out + orow * D;
+  if constexpr (kVec) {
 #pragma unroll
-  for (int k = 0; k < kMaxPerLane; ++k) {
-    const int d = lane + 64 * k;
-    if (d < D) out[orow * D + d] = (n > 0 && den > 0.f) ? acc[k] / den : 0.f;
+    for (int k = 0; k < kPer / 4; ++k) {
+      const int d = 4 * j + 64 * k;
+      if (d < D)
+        *reinterpret_cast<float4*>(dst + d) =
+            any ? make_float4(acc[4 * k] / den, acc[4 * k + 1] / den, acc[4 * k + 2] / den,
+                              acc[4 * k + 3] / den)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int d = j + kRedLanes * k;
+      if (d < D) dst[d] = any ? acc[k] / den : 0.f;
+    }
   }
 }
 
@@ -262,10 +312,19 @@ hipError_t launch_reduce(float* out, const float* max_logits, const float* exp_s
                          hipStream_t stream) {
   (void)partition_size;
   const int64_t units = static_cast<int64_t>(num_seqs) * num_heads;
-  const unsigned blocks = static_cast<unsigned>((units + kRedWaves - 1) / kRedWaves);
-  reduce_kernel<<<blocks, kRedWaves * 64, 0, stream>>>(out, max_logits, exp_sums, tmp_out,
-                                                       context_lens, num_seqs, num_heads,
-                                                       head_size, max_partitions);
+  constexpr int per_block = kRedWaves * kRedUnits;
+  const unsigned blocks = static_cast<unsigned>((units + per_block - 1) / per_block);
+  // the float4 path needs 16-byte aligned rows
+  const bool vec = head_size % 64 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(tmp_out)) & 15) == 0;
+  if (vec)
+    reduce_kernel<true><<<blocks, kRedWaves * 64, 0, stream>>>(
+        out, max_logits, exp_sums, tmp_out, context_lens, num_seqs, num_heads, head_size,
+        max_partitions);
+  else
+    reduce_kernel<false><<<blocks, kRedWaves * 64, 0, stream>>>(
+        out, max_logits, exp_sums, tmp_out, context_lens, num_seqs, num_heads, head_size,
+        max_partitions);
   return hipGetLastError();
 }
 
