@@ -210,3 +210,107 @@ def test_swap_refuses_pageable_memory(dev, pkv):
     pkv.paged_kv_swap_out(good, ks, vs, ids)
     torch.cuda.synchronize()
     assert torch.equal(good[0, 0].view(torch.int16), ks[0][:2].cpu().view(torch.int16))
+
+
+# ---- full sizes, in the configuration the bench times ---------------------------------
+
+def _pattern(ids, layer, kv, elems):
+    """Distinct 16-bit patterns per (block, layer, K/V, element), made on the
+    device (only bits matter: the moves are bit copies)."""
+    base = ((ids.to(torch.int64) * 40503 + layer * 1009 + kv * 7) % 65536).to(torch.int32)
+    e = torch.arange(elems, device=ids.device, dtype=torch.int32) * 3
+    return ((base[:, None] + e[None, :]) % 65536 - 32768).to(torch.int16)
+
+
+def test_copy_blocks_full_size(dev, pkv):
+    """The parallel-sampling workload at full size (128 prompts x 4 branches,
+    32 layers, one call over all layers through a PoolSet, as the bench runs
+    it): every pair's destination equals its source in every layer's K and V
+    pool and every other block is untouched; layers 0 and 31 against the
+    oracle's block copy, whole pools."""
+    torch.cuda.empty_cache()
+    b = W.cow_fork_bf16()
+    L = b.num_layers
+    shape = (b.num_blocks, b.num_kv_heads, b.block_size, b.head_size)
+    elems = shape[1] * shape[2] * shape[3]
+    say(f"case: copy blocks full size, {L} layers x {shape}, {len(b.copy_pairs)} pairs")
+    all_ids = torch.arange(b.num_blocks, device=dev)
+    ks, vs = [], []
+    for l in range(L):
+        for kv, lst in ((0, ks), (1, vs)):
+            t = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+            t.view(torch.int16).view(b.num_blocks, elems).copy_(_pattern(all_ids, l, kv, elems))
+            lst.append(t)
+    sampled = {l: (_raw(ks[l], "bf16"), _raw(vs[l], "bf16")) for l in (0, L - 1)}
+    pairs = [(int(s), int(d)) for s, d in b.copy_pairs]
+    pools = pkv.PoolSet(ks, vs)
+    pkv.paged_kv_copy_blocks(pools, None, torch.as_tensor(b.copy_pairs, dtype=torch.int64,
+                                                          device=dev))
+    torch.cuda.synchronize()
+    src = torch.as_tensor([p[0] for p in pairs], device=dev)
+    dst = torch.as_tensor([p[1] for p in pairs], device=dev)
+    other = torch.ones(b.num_blocks, dtype=torch.bool, device=dev)
+    other[dst] = False
+    for l in range(L):
+        for kv, t in ((0, ks[l]), (1, vs[l])):
+            bits = t.view(torch.int16).view(b.num_blocks, elems)
+            assert torch.equal(bits[dst], _pattern(src, l, kv, elems)), (l, kv)
+            assert torch.equal(bits[other], _pattern(all_ids[other], l, kv, elems)), (l, kv)
+    for l, (k0, v0) in sampled.items():
+        assert np.array_equal(_raw(ks[l], "bf16"), oracle.scatter.copy_blocks(k0, pairs))
+        assert np.array_equal(_raw(vs[l], "bf16"), oracle.scatter.copy_blocks(v0, pairs))
+    del ks, vs, pools
+    torch.cuda.empty_cache()
+
+
+def test_swap_full_size(dev, pkv):
+    """The bench's swap: 8 sequences of the 32-layer decode step (pools of
+    73740 blocks, 2.4 GB each: offsets beyond 2^31) out to one pinned buffer
+    and back into a shuffle of spare and freed blocks. The pools are left
+    uninitialised except for the swapped blocks (the kernels read nothing
+    else); every host slab and every restored block is compared bit for bit,
+    and sampled other blocks are untouched."""
+    torch.cuda.empty_cache()
+    b = W.decode_step_bf16()
+    L = b.num_layers
+    shape = (b.num_blocks, b.num_kv_heads, b.block_size, b.head_size)
+    elems = shape[1] * shape[2] * shape[3]
+    rng = np.random.default_rng(17)
+    victims = np.sort(rng.choice(b.num_seqs, 8, replace=False))
+    ids = [int(x) for s in victims for x in b.block_table[s] if x >= 0]
+    keep = set(int(x) for s in range(b.num_seqs) if s not in set(victims.tolist())
+               for x in b.block_table[s] if x >= 0)
+    free = np.array([x for x in range(b.num_blocks) if x not in keep], np.int64)
+    fresh = [int(x) for x in rng.permutation(free)[:len(ids)]]
+    say(f"case: swap full size, {L} layers x {shape}, {len(ids)} blocks")
+    ids_t = torch.as_tensor(ids, dtype=torch.int64, device=dev)
+    fresh_t = torch.as_tensor(fresh, dtype=torch.int64, device=dev)
+    untouched = torch.as_tensor(sorted(set(rng.choice(b.num_blocks, 64, replace=False).tolist())
+                                       - set(fresh)), dtype=torch.int64, device=dev)
+    ks, vs, snap = [], [], []
+    for l in range(L):
+        for kv, lst in ((0, ks), (1, vs)):
+            t = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+            bits = t.view(torch.int16).view(b.num_blocks, elems)
+            bits[ids_t] = _pattern(ids_t, l, kv, elems)
+            snap.append(bits[untouched].clone())
+            lst.append(t)
+    buf = torch.empty((L, 2, len(ids)) + shape[1:], dtype=torch.bfloat16, pin_memory=True)
+    pools = pkv.PoolSet(ks, vs)
+    pkv.paged_kv_swap_out(buf, pools, None, ids_t)
+    torch.cuda.synchronize()
+    for l in range(L):
+        for kv in (0, 1):
+            got = buf[l, kv].view(torch.int16).reshape(len(ids), elems).to(dev)
+            assert torch.equal(got, _pattern(ids_t, l, kv, elems)), ("out", l, kv)
+    pkv.paged_kv_swap_in(buf, pools, None, fresh_t)
+    torch.cuda.synchronize()
+    i = 0
+    for l in range(L):
+        for kv, t in ((0, ks[l]), (1, vs[l])):
+            bits = t.view(torch.int16).view(b.num_blocks, elems)
+            assert torch.equal(bits[fresh_t], _pattern(ids_t, l, kv, elems)), ("in", l, kv)
+            assert torch.equal(bits[untouched], snap[i]), ("untouched", l, kv)
+            i += 1
+    del ks, vs, pools, buf, snap
+    torch.cuda.empty_cache()
