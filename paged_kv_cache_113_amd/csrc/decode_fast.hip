@@ -95,11 +95,9 @@ struct Geo {
     const int64_t base = (blk < 0 ? 0 : blk) * block_stride + kvh * head_stride +
                          static_cast<int64_t>(tok0 % B) * kD * 2;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      t.k[kk] = *reinterpret_cast<const uint4*>(kc + base + k_off + kk * 64);
+    for (int kk = 0; kk < 4; ++kk) t.k[kk] = stream_load(kc + base + k_off + kk * 64);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      t.v[i] = *reinterpret_cast<const uint4*>(vc + base + v_off + i * 256);
+    for (int i = 0; i < 4; ++i) t.v[i] = stream_load(vc + base + v_off + i * 256);
     return blk >= 0;
   }
 };
@@ -231,8 +229,11 @@ struct Cursor {
 
 template <typename T, bool kVar>
 __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs a,
-                                                                     int waves_per_kv) {
-  extern __shared__ int s_pre[];  // [S + 1]: tiles before sequence s
+                                                                     int waves_per_kv,
+                                                                     int stage_bytes) {
+  // dynamic LDS: the tile prefix [S + 1], then one staging area of
+  // stage_bytes per wave for finished pieces
+  extern __shared__ __attribute__((aligned(16))) int s_pre[];  // [S + 1]: tiles before sequence s
   __shared__ __attribute__((aligned(16))) char s_slots[(kSplitThreads / 64) * kSlotBytes];
   __shared__ int s_max[kSplitThreads / 64];
   __shared__ int s_wsum[kSplitThreads / 64];
@@ -472,33 +473,119 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   Attend<T> st;
   st.reset();
 
-  // write this piece's partial; after a unit's last piece, mark the remaining
-  // slots unused (l = 0) so the merge skips them
+  // Finished pieces. A piece's partial (m, l and the normalised output of its
+  // live columns) waits in this wave's LDS staging area and is written to the
+  // workspace when the wave's range ends, or earlier when the area is full:
+  // stores spread through the KV stream slow down the loads of the whole GPU
+  // (a few MB of partials cost several percent of the stream's time), while
+  // the same stores issued in one burst at the end of the range do not. A
+  // unit's last piece also marks its remaining slots unused (l = 0) so the
+  // merge skips them. Live columns are a prefix [0, nl) of the 16 columns.
+  //
+  // Record: int4 header {sequence (decode) or first query row, column group,
+  // slot, nl | mark << 16}, then nl rows of 128 floats, then nl (m, l) pairs.
+  PKV_LDS char* stage = (PKV_LDS char*)(s_pre) +
+                        ((static_cast<int>(sizeof(int)) * (S + 1) + 15) & ~15) + w * stage_bytes;
+  int st_used = 0, st_n = 0;  // bytes and records staged (wave-uniform)
+  auto live_cols = [&](const Cursor& c) {
+    if constexpr (kVar) {
+      int k = c.qn - c.c * tpg;
+      k = k < tpg ? k : tpg;
+      return k > 0 ? k * G : 0;
+    }
+    return G;
+  };
+  // workspace row (query row x heads + head) of column n of a piece
+  auto row_index = [&](int sq, int cg, int n) -> int64_t {
+    if constexpr (kVar)
+      return static_cast<int64_t>(sq + cg * tpg + n / G) * a.num_heads + kvh * G + n % G;
+    return static_cast<int64_t>(sq) * a.num_heads + kvh * G + n;
+  };
+  auto rec_bytes = [](int nl) { return (16 + nl * (kD * 4 + 8) + 15) & ~15; };
+  // A unit's last piece marks slots piece+1 .. mp-1 of its nl rows unused.
+  auto mark_rest = [&](int sq, int cg, int pc, int nl) {
+    const int rest = mp - pc - 1;
+    for (int idx = lane; idx < nl * rest; idx += 64) {
+      const int r = idx / rest;
+      const int64_t e = row_index(sq, cg, r) * mp + pc + 1 + idx % rest;
+      store_untracked(a.max_logits + e, -INFINITY);
+      store_untracked(a.exp_sums + e, 0.f);
+    }
+  };
+  // Write every staged record: two 512-byte rows per store instruction.
+  auto flush = [&]() {
+    int off = 0;
+    for (int k = 0; k < st_n; ++k) {
+      const PKV_LDS char* rec = stage + off;
+      const u32x4 h = *(const PKV_LDS u32x4*)(rec);
+      const int sq = __builtin_amdgcn_readfirstlane(static_cast<int>(h[0]));
+      const int cg = __builtin_amdgcn_readfirstlane(static_cast<int>(h[1]));
+      const int pc = __builtin_amdgcn_readfirstlane(static_cast<int>(h[2]));
+      const int nl = __builtin_amdgcn_readfirstlane(static_cast<int>(h[3] & 0xffffu));
+      const int mark = __builtin_amdgcn_readfirstlane(static_cast<int>(h[3] >> 16));
+      if (pc < mp) {
+        for (int r0 = 0; r0 < nl; r0 += 2) {
+          const int r = r0 + (lane >> 5);
+          const int ch = lane & 31;
+          if (r < nl) {
+            const f32x4 v = *(const PKV_LDS f32x4*)(rec + 16 + r * (kD * 4) + ch * 16);
+            store_untracked(a.tmp_out + (row_index(sq, cg, r) * mp + pc) * kD + ch * 4,
+                            make_float4(v[0], v[1], v[2], v[3]));
+          }
+        }
+        if (lane < nl) {
+          const f32x2 ml = *(const PKV_LDS f32x2*)(rec + 16 + nl * (kD * 4) + lane * 8);
+          const int64_t e = row_index(sq, cg, lane) * mp + pc;
+          store_untracked(a.max_logits + e, ml[0]);
+          store_untracked(a.exp_sums + e, ml[1]);
+        }
+      }
+      if (mark) mark_rest(sq, cg, pc, nl);
+      off += rec_bytes(nl);
+    }
+    st_used = 0;
+    st_n = 0;
+  };
   auto finish = [&](const Cursor& c) {
     const float l_col = st.column_sum();
-    const int64_t prow = kVar ? static_cast<int64_t>(c.q0 + lane_token(c)) * a.num_heads +
-                                    kvh * G + my_g
-                              : static_cast<int64_t>(c.s) * a.num_heads + kvh * G + col;
-    if (kVar ? lane_live(c) : my_col) {
-      if (piece < mp) {
-        const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
-        float* dst = a.tmp_out + (prow * mp + piece) * kD + 4 * grp;
+    const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
+    const int nl = live_cols(c);
+    const int sq = kVar ? c.q0 : c.s;
+    const int cg = kVar ? c.c : 0;
+    const bool last = c.t == c.n - 1;
+    const int need = rec_bytes(nl);
+    if (st_used + need > stage_bytes) flush();
+    if (need <= stage_bytes) {
+      PKV_LDS char* rec = stage + st_used;
+      if (col < nl) {
+        PKV_LDS char* ob = rec + 16 + col * (kD * 4) + grp * 16;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) *(PKV_LDS f32x4*)(ob + db * 64) = st.acc[db] * inv;
+        if (grp == 0)  // natural-log units
+          *(PKV_LDS f32x2*)(rec + 16 + nl * (kD * 4) + col * 8) = f32x2{st.m_run * kLn2, l_col};
+      }
+      if (lane == 0)
+        *(PKV_LDS u32x4*)(rec) = u32x4{static_cast<unsigned>(sq), static_cast<unsigned>(cg),
+                                       static_cast<unsigned>(piece),
+                                       static_cast<unsigned>(nl | (last << 16))};
+      st_used += need;
+      ++st_n;
+    } else {
+      // no room even in an empty area: write directly
+      if (col < nl && piece < mp) {
+        float* dst = a.tmp_out + (row_index(sq, cg, col) * mp + piece) * kD + 4 * grp;
 #pragma unroll
         for (int db = 0; db < 8; ++db)
-          *reinterpret_cast<float4*>(dst + 16 * db) =
-              make_float4(st.acc[db][0] * inv, st.acc[db][1] * inv, st.acc[db][2] * inv,
-                          st.acc[db][3] * inv);
+          store_untracked(dst + 16 * db,
+                          make_float4(st.acc[db][0] * inv, st.acc[db][1] * inv,
+                                      st.acc[db][2] * inv, st.acc[db][3] * inv));
         if (grp == 0) {
-          a.max_logits[prow * mp + piece] = st.m_run * kLn2;  // natural-log units
-          a.exp_sums[prow * mp + piece] = l_col;
+          const int64_t e = row_index(sq, cg, col) * mp + piece;
+          store_untracked(a.max_logits + e, st.m_run * kLn2);
+          store_untracked(a.exp_sums + e, l_col);
         }
       }
-      if (c.t == c.n - 1 && grp == 0) {
-        for (int p = piece + 1; p < mp; ++p) {
-          a.max_logits[prow * mp + p] = -INFINITY;
-          a.exp_sums[prow * mp + p] = 0.f;
-        }
-      }
+      if (last) mark_rest(sq, cg, piece, nl);
     }
     st.reset();
     piece = 0;
@@ -541,44 +628,61 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     if (!step(ta, ga, tb, gb)) break;
     if (!step(tb, gb, ta, ga)) break;
   }
+  flush();
 }
 
-// Resident workgroups of the split kernel on one device, for a given
-// dynamic LDS size class. Computed on first use and kept: the answer only
-// depends on the device and the kernel, and the query costs host time that
-// would otherwise sit between back-to-back launches.
+// Launch shape of the split kernel on one device: the resident workgroups
+// and the dynamic LDS each one takes. The kernel is register-bound at
+// kResidentPerCu workgroups per CU; its dynamic LDS (tile prefix + staging
+// areas) takes whatever that leaves of the CU's LDS. Computed on first use
+// and kept: the answer only depends on the device and the kernel, and the
+// queries cost host time that would otherwise sit between back-to-back
+// launches.
 constexpr int kMaxDevices = 64;
-constexpr int kLdsClasses = 4;  // prefix sizes up to 2, 8, 16, 33 KiB
+constexpr int kResidentPerCu = 2;
 
-inline int lds_class(size_t dyn) {
-  return dyn <= 2048 ? 0 : dyn <= 8192 ? 1 : dyn <= 16384 ? 2 : 3;
-}
-inline size_t lds_class_bytes(int c) {
-  const size_t b[kLdsClasses] = {2048, 8192, 16384, (kMaxSeqsBalanced + 1) * sizeof(int)};
-  return b[c];
-}
+struct SplitShape {
+  int cus, per_cu;
+  size_t dyn;
+};
 
 template <typename T, bool kVar>
-hipError_t split_grid(int& cus, int& per_cu, size_t dyn) {
-  static std::atomic<int> cache[kMaxDevices][kLdsClasses][2];  // 0 = not computed yet
+hipError_t split_shape(SplitShape& out) {
+  static std::atomic<int> cache[kMaxDevices][3];  // cus, per_cu, dyn; 0 = not computed yet
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  const int c = lds_class(dyn);
-  if (dev >= 0 && dev < kMaxDevices) {
-    cus = cache[dev][c][0].load(std::memory_order_relaxed);
-    per_cu = cache[dev][c][1].load(std::memory_order_relaxed);
-    if (cus > 0 && per_cu > 0) return hipSuccess;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    out.cus = cache[dev][0].load(std::memory_order_relaxed);
+    out.per_cu = cache[dev][1].load(std::memory_order_relaxed);
+    out.dyn = static_cast<size_t>(cache[dev][2].load(std::memory_order_relaxed));
+    if (out.cus > 0 && out.per_cu > 0 && out.dyn > 0) return hipSuccess;
   }
+  auto kernel = decode_split_kernel<T, kVar>;
+  int cus = 0, lds_cu = 0, per_cu = 0;
+  hipFuncAttributes fa;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<T, kVar>,
-                                                     kSplitThreads, lds_class_bytes(c));
+    e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+  if (e == hipSuccess) e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kernel));
+  if (e != hipSuccess) return e;
+  // the prefix alone must always fit
+  const size_t need = ((static_cast<size_t>(kMaxSeqsBalanced) + 1) * sizeof(int) + 15) & ~size_t(15);
+  size_t dyn = static_cast<size_t>(lds_cu) / kResidentPerCu;
+  dyn = dyn > fa.sharedSizeBytes + 1024 ? (dyn - fa.sharedSizeBytes - 1024) & ~size_t(1023) : 0;
+  if (dyn < need) dyn = need;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dyn));
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kSplitThreads, dyn);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
-  if (dev >= 0 && dev < kMaxDevices) {
-    cache[dev][c][1].store(per_cu, std::memory_order_relaxed);
-    cache[dev][c][0].store(cus, std::memory_order_relaxed);
+  out = SplitShape{cus, per_cu, dyn};
+  if (cached) {
+    cache[dev][2].store(static_cast<int>(dyn), std::memory_order_relaxed);
+    cache[dev][1].store(per_cu, std::memory_order_relaxed);
+    cache[dev][0].store(cus, std::memory_order_relaxed);
   }
   return hipSuccess;
 }
@@ -586,18 +690,20 @@ hipError_t split_grid(int& cus, int& per_cu, size_t dyn) {
 template <typename T, bool kVar>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
   auto kernel = decode_split_kernel<T, kVar>;
-  const size_t dyn = static_cast<size_t>(a.num_seqs + 1) * sizeof(int);
-  int cus = 0, per_cu = 0;
-  hipError_t e = split_grid<T, kVar>(cus, per_cu, dyn);
+  SplitShape sh{};
+  hipError_t e = split_shape<T, kVar>(sh);
   if (e != hipSuccess) return e;
   const int waves_per_wg = kSplitThreads / 64;
+  // staging area per wave: what the prefix leaves, in whole 16-byte units
+  const size_t pre = (static_cast<size_t>(a.num_seqs + 1) * sizeof(int) + 15) & ~size_t(15);
+  const int stage = static_cast<int>(((sh.dyn - pre) / waves_per_wg) & ~size_t(15));
   // whole groups of num_kv_heads waves, no more than the GPU holds at once
-  int64_t waves = static_cast<int64_t>(cus) * per_cu * waves_per_wg;
+  int64_t waves = static_cast<int64_t>(sh.cus) * sh.per_cu * waves_per_wg;
   int64_t per_kv = waves / a.num_kv_heads;
   if (per_kv < 1) per_kv = 1;
   const int64_t wgs = (per_kv * a.num_kv_heads + waves_per_wg - 1) / waves_per_wg;
-  kernel<<<dim3(static_cast<unsigned>(wgs)), dim3(kSplitThreads), dyn, stream>>>(
-      a, static_cast<int>(per_kv));
+  kernel<<<dim3(static_cast<unsigned>(wgs)), dim3(kSplitThreads), sh.dyn, stream>>>(
+      a, static_cast<int>(per_kv), stage);
   return hipGetLastError();
 }
 
