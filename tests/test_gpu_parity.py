@@ -326,3 +326,47 @@ def test_split_slots_contract(dev, pkv, name, P, mp_override):
     e = max_err(out.cpu(), want)
     say(f"  max abs err {e:.3e}, pieces per (seq, head) up to {int(used.sum(-1).max())}")
     assert e <= TOL
+
+
+MANY = {
+    # ~16 short sequences per wave and KV head: finished pieces outgrow a
+    # wave's LDS staging area and are flushed before the wave's range ends
+    "short_gqa4_s4000": lambda: W._uniform_case("short_gqa4", "bf16", 32, 8, 128, 16, 4000, 1,
+                                                40, 91),
+    # the largest batch the split kernel takes with a group of 16 heads: the
+    # prefix leaves less staging room than one piece needs, pieces go out
+    # directly
+    "short_gqa16_s8192": lambda: W._uniform_case("short_gqa16", "f16", 32, 2, 128, 16, 8192, 1,
+                                                 40, 92),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MANY))
+def test_split_many_pieces_per_wave(dev, pkv, name):
+    """Many short sequences in split mode: every (sequence, head) within
+    2e-3 of the oracle, every slot a partial (l >= 1) or marked unused."""
+    b = MANY[name]()
+    P = 16
+    mp = b.max_partitions(P)
+    say(f"case: many pieces {name} S={b.num_seqs} G={b.num_heads // b.num_kv_heads} mp={mp}")
+    t = W.layer_tensors(b, device=dev)
+    meta = device_meta(b, dev)
+    shape = (b.num_seqs, b.num_heads, mp)
+    ml = torch.full(shape, float("nan"), device=dev)
+    es = torch.full(shape, float("nan"), device=dev)
+    to = torch.full(shape + (b.head_size,), float("nan"), device=dev)
+    pkv.paged_decode_attention(None, t["q"], t["k_cache"], t["v_cache"], meta["table"],
+                               meta["ctx"], scale_of(b), P, mp, ml, es, to)
+    out = torch.empty(b.num_seqs, b.num_heads, b.head_size, device=dev)
+    pkv.paged_attention_reduce(out, ml, es, to, meta["ctx"], P)
+    torch.cuda.synchronize()
+    es, ml = es.cpu(), ml.cpu()
+    assert not torch.isnan(es).any() and not torch.isnan(ml).any()
+    used = es > 0
+    assert (es[used] >= 1.0 - 1e-6).all()
+    assert torch.isinf(ml[~used]).all() and (used.sum(-1) >= 1).all()
+    th = host(t)
+    want = oracle_attention(b, th["q"], th["k_cache"], th["v_cache"])
+    e = max_err(out.cpu(), want)
+    say(f"  max abs err {e:.3e}")
+    assert e <= TOL

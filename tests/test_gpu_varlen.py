@@ -56,14 +56,22 @@ SMALL = {
     # MHA: chunks of 128+ tokens reach the prefill kernel (one head per KV head)
     "f16_mha_long": lambda: _mix("f16_mha_long", "f16", 4, 4, 128, 16, 208, n=6,
                                  kinds=[1, 130, 4, 200, 127, 257]),
+    # 3000 speculative groups of 4 tokens on short histories: every piece
+    # fills all 16 columns and the LDS staging area holds one at a time
+    "bf16_g4_spec_many": lambda: W._varlen_case(
+        "bf16_g4_spec_many", "bf16", 32, 8, 128, 16,
+        np.random.default_rng(209).integers(0, 60, size=3000, endpoint=True),
+        np.full(3000, 4), 209),
 }
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_varlen_small(dev, pkv, name):
     b = SMALL[name]()
-    say(f"case: varlen {name} S={b.num_seqs} T={b.num_tokens} "
-        f"q={b.query_lens.tolist()} ctx={b.context_lens.tolist()}")
+    detail = (f"q={b.query_lens.tolist()} ctx={b.context_lens.tolist()}" if b.num_seqs <= 64
+              else f"q {b.query_lens.min()}..{b.query_lens.max()} "
+                   f"ctx {b.context_lens.min()}..{b.context_lens.max()}")
+    say(f"case: varlen {name} S={b.num_seqs} T={b.num_tokens} {detail}")
     t = W.layer_tensors(b, device=dev)
     meta = device_meta(b, dev)
     th = host(t)
