@@ -283,6 +283,102 @@ __global__ __launch_bounds__(kRedWaves * 64) void reduce_kernel(
   }
 }
 
+// Merge with many slots per row: one wave per (row, head), so that the
+// pieces of a long context (tens of them per row) are read with many loads
+// in flight instead of a few per 16-lane unit. The wave reads 64 slots'
+// (m, l) at a time; each output row o_p is read by D/4 lanes, 16 bytes each,
+// so one load instruction covers 256/D slots, and eight of them are in
+// flight per round. Sums are fp32 as in reduce_kernel (only their order
+// differs).
+template <int D>
+__global__ __launch_bounds__(kRedWaves * 64) void reduce_row_kernel(
+    float* __restrict__ out, const float* __restrict__ max_logits,
+    const float* __restrict__ exp_sums, const float* __restrict__ tmp_out,
+    const int32_t* __restrict__ context_lens, int num_seqs, int num_heads,
+    int max_partitions) {
+  constexpr int kLps = D / 4;      // lanes per slot row
+  constexpr int kSps = 64 / kLps;  // slots per load instruction
+  constexpr int kBatch = 8;        // load instructions in flight per round
+  constexpr int kPick = kBatch * kSps;
+  const int lane = threadIdx.x & 63;
+  const int64_t total = static_cast<int64_t>(num_seqs) * num_heads;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRedWaves +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (row >= total) return;  // the whole wave
+  const int seq = static_cast<int>(row / num_heads);
+  const int mp = max_partitions;
+  const int n = (context_lens == nullptr || read_only(context_lens + seq) > 0) ? mp : 0;
+  const float* __restrict__ m = max_logits + row * mp;
+  const float* __restrict__ l = exp_sums + row * mp;
+  const float* __restrict__ o = tmp_out + row * mp * D;
+
+  float mx = -INFINITY;
+  for (int p = lane; p < n; p += 64)
+    if (l[p] > 0.f) mx = fmaxf(mx, m[p]);
+  const float M = wave_max(mx);
+
+  const int my_s = lane / kLps;      // which of the instruction's slots
+  const int my_d = 4 * (lane % kLps);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  for (int c0 = 0; c0 < n; c0 += 64) {  // uniform over the wave
+    const int p = c0 + lane;
+    float wp = 0.f;
+    if (p < n) {
+      const float lp = l[p];
+      wp = lp > 0.f ? lp * expf(m[p] - M) : 0.f;
+    }
+    den += wp;
+    uint64_t used = __ballot(wp != 0.f);
+    while (used) {
+      // the next kPick used slots of the chunk, in order (-1: none)
+      int pick[kPick];
+#pragma unroll
+      for (int i = 0; i < kPick; ++i) {
+        pick[i] = used ? static_cast<int>(__builtin_ctzll(used)) : -1;
+        used &= used ? used - 1 : 0;
+      }
+      int b[kBatch];
+      float wb[kBatch];
+      float4 v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        int x = pick[k * kSps];
+#pragma unroll
+        for (int t = 1; t < kSps; ++t) x = my_s == t ? pick[k * kSps + t] : x;
+        b[k] = x;
+        wb[k] = __shfl(wp, x < 0 ? 0 : x, 64);
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        v[k] = b[k] >= 0 ? *reinterpret_cast<const float4*>(o + static_cast<int64_t>(c0 + b[k]) * D + my_d)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const float w = b[k] >= 0 ? wb[k] : 0.f;
+        acc.x = fmaf(w, v[k].x, acc.x);
+        acc.y = fmaf(w, v[k].y, acc.y);
+        acc.z = fmaf(w, v[k].z, acc.z);
+        acc.w = fmaf(w, v[k].w, acc.w);
+      }
+    }
+  }
+  // lanes holding the same dims (one per slot of an instruction) add up
+#pragma unroll
+  for (int off = kLps; off < 64; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off, 64);
+    acc.y += __shfl_xor(acc.y, off, 64);
+    acc.z += __shfl_xor(acc.z, off, 64);
+    acc.w += __shfl_xor(acc.w, off, 64);
+  }
+  den = wave_sum(den);
+  if (my_s != 0) return;
+  const bool any = n > 0 && den > 0.f;
+  *reinterpret_cast<float4*>(out + row * D + my_d) =
+      any ? make_float4(acc.x / den, acc.y / den, acc.z / den, acc.w / den)
+          : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 }  // namespace
 
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream) {
@@ -317,6 +413,20 @@ hipError_t launch_reduce(float* out, const float* max_logits, const float* exp_s
   // the float4 path needs 16-byte aligned rows
   const bool vec = head_size % 64 == 0 &&
                    ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(tmp_out)) & 15) == 0;
+  // more slots than one 16-lane round covers: a wave per row
+  if (vec && max_partitions > kRedLanes && (head_size == 64 || head_size == 128 ||
+                                            head_size == 256)) {
+    const unsigned rb = static_cast<unsigned>((units + kRedWaves - 1) / kRedWaves);
+#define PKV_ROW(DD)                                                                          \
+  reduce_row_kernel<DD><<<rb, kRedWaves * 64, 0, stream>>>(out, max_logits, exp_sums, tmp_out, \
+                                                          context_lens, num_seqs, num_heads,  \
+                                                          max_partitions)
+    if (head_size == 64) PKV_ROW(64);
+    else if (head_size == 128) PKV_ROW(128);
+    else PKV_ROW(256);
+#undef PKV_ROW
+    return hipGetLastError();
+  }
   if (vec)
     reduce_kernel<true><<<blocks, kRedWaves * 64, 0, stream>>>(
         out, max_logits, exp_sums, tmp_out, context_lens, num_seqs, num_heads, head_size,

@@ -169,6 +169,28 @@ def test_reduce_random_partials(dev, pkv):
     assert e <= 1e-5
 
 
+@pytest.mark.parametrize("D,mp", [(64, 40), (128, 300), (256, 17), (128, 64)])
+def test_reduce_many_slots(dev, pkv, D, mp):
+    """More slots per row than one 16-lane round covers (the wave-per-row
+    merge): rows with 0, 1, a few, more than 64 and all slots live, NaN in
+    the others, against the oracle's log-sum-exp merge."""
+    say(f"case: reduce with many slots D={D} mp={mp}")
+    Psz = 16
+    ctx = np.array([0, 1, 17 * Psz, min(mp, 70) * Psz - 5, mp * Psz, 33 * Psz + 1], np.int32)
+    S, H = len(ctx), 3
+    m, l, o = W.random_partials(S, H, D, mp, ctx, Psz, seed=D + mp)
+    out = torch.empty(S, H, D, device=dev)
+    pkv.paged_attention_reduce(out, m.to(dev), l.to(dev), o.to(dev),
+                               torch.as_tensor(ctx, device=dev), Psz)
+    torch.cuda.synchronize()
+    want = oracle.lse_combine(m.double().numpy(), l.double().numpy(), o.double().numpy(),
+                              np.minimum(ctx, mp * Psz), Psz)
+    e = max_err(out.cpu(), want)
+    say(f"  max abs err {e:.3e}")
+    assert e <= 1e-5
+    assert (out[0] == 0).all()
+
+
 def test_block_permutation_is_bitwise_invariant(dev, pkv):
     """Moving physical blocks (and rewriting the table) must not change one
     output bit: the kernels see the same data in the same order."""
