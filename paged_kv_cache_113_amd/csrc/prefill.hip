@@ -50,7 +50,8 @@ constexpr int kGroupsPerWave = 2;                          // 2 x 16 columns
 constexpr int kGroupsPerUnit = kPfWaves * kGroupsPerWave;  // 128 columns
 constexpr int kStage = 64;                                 // positions per stage
 constexpr int kSub = kStage / kTile;                       // 16-row blocks per stage
-constexpr int kKRow = kD * 2 + 16;                         // K row pitch in LDS
+constexpr int kStageBytes = kStage * kD * 2;               // K or V rows of a stage
+constexpr int kPreInts = 4 * kStageBytes / 4;              // dynamic LDS ints before the prefix
 constexpr int kMaxSeqsPrefill = 8192;                      // LDS prefix capacity
 constexpr int kXcdCount = 8;                               // MI355X: 8 XCDs
 
@@ -117,9 +118,9 @@ __device__ __forceinline__ int unit_stages(int ctx, int qn, int u, int per) {
 
 template <typename T>
 __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a, int wgs_per_kv) {
-  extern __shared__ int s_pre[];  // [S + 1]: stages of units before sequence s
-  __shared__ __attribute__((aligned(16))) char s_k[kStage * kKRow];
-  __shared__ __attribute__((aligned(16))) char s_v[kStage * kSlotRow];
+  // dynamic LDS: two stage buffers (K rows, then V rows, kStageBytes each),
+  // then the prefix [S + 1]: stages of units before sequence s
+  extern __shared__ __attribute__((aligned(16))) int s_dyn[];
   __shared__ int s_max[kPfWaves];
   __shared__ int s_wsum[kPfWaves];
   const int tid = threadIdx.x;
@@ -196,12 +197,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
     for (int i = 0; i < per; ++i) {
       const int s = s_lo + i;
       if (s < S) {
-        s_pre[s] = run;
+        s_dyn[kPreInts + s] = run;
         int last;
         run += seq_stages(s, last);
       }
     }
-    if (tid == 0) s_pre[S] = T1;
+    if (tid == 0) s_dyn[kPreInts + S] = T1;
   }
   __syncthreads();
   T1 = __builtin_amdgcn_readfirstlane(T1);
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
   auto range_of = [&](int x) {
     return static_cast<int>(((static_cast<int64_t>(x) + 1) * Wk - 1) / T1);
   };
-  auto pre = [&](int s) { return __builtin_amdgcn_readfirstlane(s_pre[s]); };
+  auto pre = [&](int s) { return __builtin_amdgcn_readfirstlane(s_dyn[kPreInts + s]); };
   int lo = 0, hi = S - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -295,29 +296,58 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
   const char* __restrict__ vc = static_cast<const char*>(a.v_cache);
   const int64_t head_stride = static_cast<int64_t>(a.block_size) * kD * 2;
   const int64_t block_stride = head_stride * a.num_kv_heads;
-  // loader lane: rows tid / 16 + 16 m (m < kSub) of the stage, chunk tid % 16
-  const int ld_row = tid >> 4;
-  const int ld_chunk = tid & 15;
   auto row_of = [&](int s) { return a.block_table + static_cast<int64_t>(s) * a.max_blocks; };
-  // global loads of a stage's K and V rows for this lane; bit m of the
-  // result says whether 16-row block m has a table entry in the pool (if
-  // not, block 0 is read instead and its rows are masked)
-  auto load_stage = [&](const PfCursor& c, uint4* kr, uint4* vr) {
+  // Stage buffers. Rows are 256 B with no padding (in-LDS loads write whole
+  // 1 KiB runs), so bank conflicts are avoided by swizzles instead: K row r
+  // keeps its 16-byte chunk c at chunk c ^ (r % 16), which spreads the 16
+  // rows of an A-operand read over all banks; V row r keeps its 32-byte
+  // segment g at segment g ^ (r % 8), which does the same for the eight rows
+  // of a transposed read.
+  auto kbuf = [&](int par) { return (PKV_LDS char*)(s_dyn) + par * (2 * kStageBytes); };
+  auto vbuf = [&](int par) { return (PKV_LDS char*)(s_dyn) + par * (2 * kStageBytes) + kStageBytes; };
+  // In-LDS loads of a stage into buffer par: wave w fills 16-row block w of
+  // the stage (K and V, four 1 KiB load instructions each); lane l of
+  // instruction j writes chunk l % 16 of block row 4j + l / 16, so it loads
+  // the global chunk the row's swizzle puts there. Returns the blocks'
+  // validity bits (bit m: block m has a table entry in the pool; if not,
+  // block 0 is read instead and its rows are masked).
+  auto dma_stage = [&](const PfCursor& c, int par) {
     int ok = 0;
+    int64_t mine = 0;
 #pragma unroll
     for (int m = 0; m < kSub; ++m) {
       const int tok0 = c.t * kStage + m * kTile;
       const int64_t blk = physical_block(row_of(c.s), tok0, a.block_size, a.max_blocks,
                                          a.num_blocks);
-      const int64_t off = (blk < 0 ? 0 : blk) * block_stride + kvh * head_stride +
-                          static_cast<int64_t>(tok0 % a.block_size + ld_row) * kD * 2 +
-                          ld_chunk * 16;
-      kr[m] = *reinterpret_cast<const uint4*>(kc + off);
-      vr[m] = *reinterpret_cast<const uint4*>(vc + off);
       ok |= (blk >= 0) << m;
+      if (m == w)
+        mine = (blk < 0 ? 0 : blk) * block_stride + kvh * head_stride +
+               static_cast<int64_t>(tok0 % a.block_size) * kD * 2;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * j + (lane >> 4);  // row within block w
+      const int cs = lane & 15;
+      const int64_t roff = mine + static_cast<int64_t>(r) * kD * 2;
+      const int at = (kTile * w + 4 * j) * kD * 2;
+      __builtin_amdgcn_global_load_lds(kc + roff + ((cs ^ r) << 4),
+                                       (PKV_LDS void*)(kbuf(par) + at), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vc + roff + ((cs ^ ((r & 7) << 1)) << 4),
+                                       (PKV_LDS void*)(vbuf(par) + at), 16, 0, 0);
     }
     return ok;
   };
+  // per-lane LDS offsets of the operand reads (rows of the first half of a
+  // stage; the second half and the second 16-row block add 8 KiB and 4 KiB)
+  int koff[4], voff[8];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = col * (kD * 2) + (((grp + 4 * kk) ^ col) << 4);
+  {
+    const int vr = 4 * grp + (col >> 2);
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      voff[db] = vr * (kD * 2) + ((db ^ (vr & 7)) << 5) + (col & 3) * 8;
+  }
   // wave-uniform V limit: positions the unit's last token sees, from the stage
   auto vlimit = [&](const PfCursor& c) {
     const int e = (c.u + 1) * utok < c.qn ? (c.u + 1) * utok : c.qn;
@@ -375,51 +405,63 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
     piece = 0;
   };
 
-  // One 32-position half h of the staged stage for the first NG groups of
-  // this wave (NG is 2, or 1 when the unit has no tokens for the second):
-  // straight-line code, no branch between the transposed reads and the
-  // matrix-core instructions that use them. masked (wave-uniform): the
-  // stage reaches past some column's causal limit or misses a block; without
-  // it every position of the stage is visible to every live column of the
-  // wave (dead columns, whose q is zero, compute finite values that are
-  // never written).
-  auto half = [&](auto ng, bool masked, int h, int ok, int stage0) {
+  // One stage of the staged buffers (kb_, vb_) for the first NG groups of
+  // this wave (NG is 2, or 1 when the unit has no tokens for the second), in
+  // three phases the compiler can overlap across groups: the scores of all
+  // 64 positions (four 16-row blocks; lane (col n, group j) gets positions
+  // 16b + 4j .. 16b + 4j + 3 of block b), one online-softmax step over the
+  // lane's 16 positions, then P.V over the two 32-position halves. masked
+  // (wave-uniform): the stage reaches past some column's causal limit or
+  // misses a block; without it every position of the stage is visible to
+  // every live column of the wave (dead columns, whose q is zero, compute
+  // finite values that are never written).
+  auto stage_math = [&](auto ng, bool masked, int ok, int stage0, const PKV_LDS char* kb_,
+                        const PKV_LDS char* vb_) {
     constexpr int NG = decltype(ng)::value;
-    // K operands of the two 16-row blocks: row 16 b + col, chunk 4 kk + grp
-    uint4 ka[4], kb[4];
-    const PKV_LDS char* kbase = (const PKV_LDS char*)s_k + (32 * h + col) * kKRow + grp * 16;
+    f32x4 S[NG][kSub];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      ka[kk] = __builtin_bit_cast(uint4, *(const PKV_LDS u32x4v*)(kbase + kk * 64));
-      kb[kk] = __builtin_bit_cast(uint4, *(const PKV_LDS u32x4v*)(kbase + 16 * kKRow + kk * 64));
+    for (int h = 0; h < 2; ++h) {
+      // K operands of the half's two 16-row blocks: row 16 b + col, chunk 4 kk + grp
+      uint4 ka[4], kb[4];
+      const PKV_LDS char* kbase = kb_ + 32 * h * (kD * 2);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        ka[kk] = __builtin_bit_cast(uint4, *(const PKV_LDS u32x4v*)(kbase + koff[kk]));
+        kb[kk] = __builtin_bit_cast(uint4, *(const PKV_LDS u32x4v*)(kbase + koff[kk] +
+                                                                     16 * (kD * 2)));
+      }
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        S[gi][2 * h] = Attend<T>::scores(ka, q[gi]);
+        S[gi][2 * h + 1] = Attend<T>::scores(kb, q[gi]);
+      }
     }
-    uint4 p_hi[NG], p_lo[NG];
+    uint4 p_hi[NG][2], p_lo[NG][2];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      const f32x4 Sa = Attend<T>::scores(ka, q[gi]);
-      const f32x4 Sb = Attend<T>::scores(kb, q[gi]);
-      float s8[8];
+      float s16[16];
       if (masked) {
-        const bool va = (ok >> (2 * h)) & 1;
-        const bool vb = (ok >> (2 * h + 1)) & 1;
-        // this column sees positions < lim of the half (relative to its start)
-        const int lim = live(cur, gi) ? cur.ctx - cur.qn + token_of(cur, gi) + 1 - stage0 - 32 * h
-                                      : 0;
+        // this column sees positions < lim of the stage (relative to its start)
+        const int lim = live(cur, gi) ? cur.ctx - cur.qn + token_of(cur, gi) + 1 - stage0 : 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s8[i] = (va && 4 * grp + i < lim) ? Sa[i] : -INFINITY;
-          s8[4 + i] = (vb && 16 + 4 * grp + i < lim) ? Sb[i] : -INFINITY;
+        for (int b = 0; b < kSub; ++b) {
+          const bool vb = (ok >> b) & 1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            s16[4 * b + i] = (vb && kTile * b + 4 * grp + i < lim) ? S[gi][b][i] : -INFINITY;
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s8[i] = Sa[i];
-          s8[4 + i] = Sb[i];
-        }
+        for (int b = 0; b < kSub; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s16[4 * b + i] = S[gi][b][i];
       }
       // the max is taken on the raw scores: scaling by qk_scale > 0 keeps it
-      float mt = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])),
-                       fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
+      float m8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m8[i] = fmaxf(s16[i], s16[8 + i]);
+      float mt = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                       fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
       mt = max_xor32(max_xor16(mt)) * qk_scale;
       const float m_old = st[gi].m_run;
       const bool move = mt > m_old + kLazyLog2;
@@ -428,12 +470,16 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
       // a column with no visible position yet keeps -inf
       const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       const float alpha = move ? fast_exp2(m_old - m_use) : 1.f;
-      float p[8];
+      float p[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(s8[i], qk_scale, -m_use));
-      st[gi].l_part = st[gi].l_part * alpha +
-                      (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-      split_p8<T>(p, p_hi[gi], p_lo[gi]);
+      for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(s16[i], qk_scale, -m_use));
+      float ps[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) ps[b] = (p[4 * b] + p[4 * b + 1]) + (p[4 * b + 2] + p[4 * b + 3]);
+      st[gi].l_part = st[gi].l_part * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+      // P of half h: blocks 2h and 2h + 1, the k order of the V^T operand
+      split_p8<T>(p, p_hi[gi][0], p_lo[gi][0]);
+      split_p8<T>(p + 8, p_hi[gi][1], p_lo[gi][1]);
       // a column with no max yet has nothing accumulated
       if (__any(move && m_old != -INFINITY)) {
 #pragma unroll
@@ -443,57 +489,60 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
     // V^T operands of the 8 dim blocks: lane (d = col, group j) takes
     // positions 4j..4j+3 of each 16-row block (the same k order as P);
     // shared by the groups
-    const PKV_LDS char* vbase = (const PKV_LDS char*)s_v +
-                                (32 * h + 4 * grp + (col >> 2)) * kSlotRow + (col & 3) * 8;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (PKV_LDS s16x4*)(vbase + 32 * db));
-      const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (PKV_LDS s16x4*)(vbase + 16 * kSlotRow + 32 * db));
-      const uint2 u0 = __builtin_bit_cast(uint2, t0);
-      const uint2 u1 = __builtin_bit_cast(uint2, t1);
-      const uint4 vt = make_uint4(u0.x, u0.y, u1.x, u1.y);
+    for (int h = 0; h < 2; ++h) {
+      const PKV_LDS char* vbase = vb_ + 32 * h * (kD * 2);
 #pragma unroll
-      for (int gi = 0; gi < NG; ++gi) {
-        st[gi].acc[db] = mfma_k32<T>(vt, p_hi[gi], st[gi].acc[db]);
-        st[gi].acc[db] = mfma_k32<T>(vt, p_lo[gi], st[gi].acc[db]);
+      for (int db = 0; db < 8; ++db) {
+        const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS s16x4*)(vbase + voff[db]));
+        const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS s16x4*)(vbase + voff[db] + 16 * (kD * 2)));
+        const uint2 u0 = __builtin_bit_cast(uint2, t0);
+        const uint2 u1 = __builtin_bit_cast(uint2, t1);
+        const uint4 vt = make_uint4(u0.x, u0.y, u1.x, u1.y);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          st[gi].acc[db] = mfma_k32<T>(vt, p_hi[gi][h], st[gi].acc[db]);
+          st[gi].acc[db] = mfma_k32<T>(vt, p_lo[gi][h], st[gi].acc[db]);
+        }
       }
     }
   };
 
-  // 3. the range, one stage at a time: barrier (every wave is done with the
-  //    LDS stage), stage i from registers into LDS (V rows past what the unit
-  //    sees are zeroed: P is 0 there and 0 * NaN would still be NaN), the
-  //    loads of stage i + 1 into the freed registers (in flight during this
-  //    stage's math), barrier, the math.
-  uint4 kr[kSub], vr[kSub];
+  // 3. the range, one stage at a time, two LDS buffers: wait for this
+  //    stage's in-LDS loads, barrier (every wave's loads of this stage have
+  //    landed and every wave is done with the other buffer), the next
+  //    stage's loads into the other buffer (in flight during this stage's
+  //    math), then the math. V rows past what the unit sees, and rows of a
+  //    block with no table entry, are zeroed first (one more barrier): P is 0
+  //    there, and 0 * NaN would still be NaN.
   load_q_unit(cur);
-  wait_all_loads();
-  int okb = load_stage(cur, kr, vr);
+  int okb = dma_stage(cur, 0);
   for (int i = 0; i < len; ++i) {
+    const int par = i & 1;
+    wait_all_loads();
     __syncthreads();
-    {
-      const int vl = vlimit(cur);
-#pragma unroll
-      for (int m = 0; m < kSub; ++m) {
-        const int row = ld_row + m * kTile;
-        uint4 v = vr[m];
-        if (row >= vl || !((okb >> m) & 1)) v = make_uint4(0, 0, 0, 0);
-        *(PKV_LDS u32x4v*)((PKV_LDS char*)s_k + row * kKRow + ld_chunk * 16) =
-            __builtin_bit_cast(u32x4v, kr[m]);
-        *(PKV_LDS u32x4v*)((PKV_LDS char*)s_v + row * kSlotRow + ld_chunk * 16) =
-            __builtin_bit_cast(u32x4v, v);
-      }
-    }
     const int ok_now = okb;
     const bool more = i + 1 < len;
     PfCursor nx = cur;
     if (more) {
       nx = advance(cur);
-      okb = load_stage(nx, kr, vr);
+      okb = dma_stage(nx, par ^ 1);
     }
-    __syncthreads();
+    {
+      const int vl = vlimit(cur);
+      if (vl < kStage || ok_now != (1 << kSub) - 1) {
+#pragma unroll
+        for (int m = 0; m < kSub; ++m) {
+          const int row = kTile * m + (tid >> 4);
+          if (row >= vl || !((ok_now >> m) & 1))
+            *(PKV_LDS u32x4v*)(vbuf(par) + row * (kD * 2) + (tid & 15) * 16) =
+                u32x4v{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+      }
+    }
     const int stage0 = cur.t * kStage;
     // the whole stage is visible to the wave's first token (the others see
     // more) and all its blocks are in the pool: no masking
@@ -502,13 +551,13 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
                           stage0 + kStage <= cur.ctx - cur.qn + first_tok + 1;
     using Two = std::integral_constant<int, 2>;
     using One = std::integral_constant<int, 1>;
+    const PKV_LDS char* kb_now = kbuf(par);
+    const PKV_LDS char* vb_now = vbuf(par);
     // groups are filled in order: the second has tokens only if the first does
     if (group_live(cur, 1)) {
-      half(Two(), !interior, 0, ok_now, stage0);
-      half(Two(), !interior, 1, ok_now, stage0);
+      stage_math(Two(), !interior, ok_now, stage0, kb_now, vb_now);
     } else if (group_live(cur, 0)) {
-      half(One(), true, 0, ok_now, stage0);
-      half(One(), true, 1, ok_now, stage0);
+      stage_math(One(), true, ok_now, stage0, kb_now, vb_now);
     }
     const bool unit_ends = cur.t + 1 >= cur.n;
     if (unit_ends || !more) finish(cur);
@@ -526,11 +575,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
 constexpr int kPfMaxDevices = 64;
 constexpr int kPfLdsClasses = 4;
 inline int pf_lds_class(size_t dyn) {
+  dyn -= 4 * static_cast<size_t>(kStageBytes);
   return dyn <= 2048 ? 0 : dyn <= 8192 ? 1 : dyn <= 16384 ? 2 : 3;
 }
 inline size_t pf_lds_class_bytes(int c) {
   const size_t b[kPfLdsClasses] = {2048, 8192, 16384, (kMaxSeqsPrefill + 1) * sizeof(int)};
-  return b[c];
+  return 4 * static_cast<size_t>(kStageBytes) + b[c];
 }
 
 template <typename T>
@@ -547,6 +597,10 @@ hipError_t prefill_grid(int& cus, int& per_cu, size_t dyn) {
   }
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_split_kernel<T>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(pf_lds_class_bytes(kPfLdsClasses - 1)));
+  if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_split_kernel<T>,
                                                      kPfThreads, pf_lds_class_bytes(c));
   if (e != hipSuccess) return e;
@@ -560,7 +614,8 @@ hipError_t prefill_grid(int& cus, int& per_cu, size_t dyn) {
 
 template <typename T>
 hipError_t launch_prefill_t(const DecodeArgs& a, hipStream_t stream) {
-  const size_t dyn = static_cast<size_t>(a.num_seqs + 1) * sizeof(int);
+  const size_t dyn = 4 * static_cast<size_t>(kStageBytes) +
+                     static_cast<size_t>(a.num_seqs + 1) * sizeof(int);
   int cus = 0, per_cu = 0;
   hipError_t e = prefill_grid<T>(cus, per_cu, dyn);
   if (e != hipSuccess) return e;
