@@ -305,6 +305,20 @@ def bench_block_moves(args):
     print(json.dumps(line), flush=True)
 
 
+def block_utilisation(batch) -> float:
+    """Live positions over the slots of the distinct blocks the tables hold
+    (nxmr.cn article, section 5.2: utilisation = live tokens / (blocks x B));
+    a block shared by several sequences counts once, its positions once."""
+    B = batch.block_size
+    live = {}
+    for s, n in enumerate(batch.context_lens):
+        n = int(n)
+        for b in range((n + B - 1) // B):
+            blk = int(batch.block_table[s, b])
+            live[blk] = max(live.get(blk, 0), min(B, n - b * B))
+    return round(sum(live.values()) / (len(live) * B), 4) if live else 0.0
+
+
 def visible_pairs(batch) -> np.ndarray:
     """Per query row, how many positions it attends (causal, new tokens at the
     end of each context): a workload statistic for the flop count."""
@@ -579,7 +593,8 @@ def main():
               "head_size": batch.head_size, "block_size": batch.block_size,
               "context_lens": f"{int(batch.context_lens.min())}..{int(batch.context_lens.max())}"
                               f" mean {float(batch.context_lens.mean()):.1f}",
-              "partition_size": P, "blocks_per_layer": batch.num_blocks}
+              "partition_size": P, "blocks_per_layer": batch.num_blocks,
+              "block_utilisation": block_utilisation(batch)}
     if varlen:
         config.update({"num_tokens": batch.num_tokens, "max_partitions": mp,
                        "query_lens": f"{int(batch.query_lens.min())}..{int(batch.query_lens.max())}"

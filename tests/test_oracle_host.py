@@ -199,3 +199,17 @@ def test_new_token_slots_take_fresh_block_on_boundary():
         if p % batch.block_size == 0:
             assert slot % batch.block_size == 0
             assert a.tables[s][-1] == slot // batch.block_size
+
+
+@pytest.mark.parametrize("make", ["tiny", "gqa_shared_bf16", "mha_fp16"])
+def test_bench_block_utilisation_matches_oracle(make):
+    """The bench line's block utilisation equals the oracle's sharing
+    statistics on the same tables (the glossary page's example: 13 live
+    positions in 16 slots)."""
+    import bench
+    b = W.CASES[make]()
+    tables = [row[row >= 0].tolist() for row in b.block_table]
+    want = A.sharing_stats(tables, b.context_lens.tolist(), b.block_size)
+    assert bench.block_utilisation(b) == round(want["utilisation"], 4)
+    if make == "tiny":
+        assert (want["live_positions"], want["allocated_slots"]) == (13, 16)
