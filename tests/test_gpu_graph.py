@@ -1,0 +1,81 @@
+"""The decode step under graph capture: slot mapping, the K/V write, split
+attention and the merge of two layers captured once in a torch CUDA graph
+(a HIP graph on ROCm) and replayed several times, with the program's own
+eager work and synchronisations between replays; every replay must equal
+the eager step bit for bit (same kernels, same launch shapes, same inputs),
+and the eager step equals the oracle within 2e-3."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_cases import (TOL, device_meta, host, max_err, oracle_attention,
+                       oracle_pools_after_write, scale_of)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def pkv(dev):
+    import paged_kv_cache_113_amd as m
+    return m
+
+
+def test_decode_step_graph_replays_equal_eager(dev, pkv):
+    b = W.decode_step_bf16(num_seqs=48, lo=1, hi=900, num_layers=2)
+    print(f"case: graph capture of a 2-layer decode step, S={b.num_seqs}", flush=True)
+    layers = [W.layer_tensors(b, layer=l, device=dev) for l in range(b.num_layers)]
+    pre = [host(t) for t in layers]
+    meta = device_meta(b, dev)
+    scale = scale_of(b)
+    P = 256
+    mp = b.max_partitions(P)
+    S, H, D = b.num_seqs, b.num_heads, b.head_size
+    slots = torch.empty(S, dtype=torch.int64, device=dev)
+    outs = [torch.empty(S, H, D, device=dev) for _ in layers]
+    ml = torch.empty(S, H, mp, device=dev)
+    es = torch.empty_like(ml)
+    to = torch.empty(S, H, mp, D, device=dev)
+
+    def step():
+        pkv.paged_slot_mapping(slots, meta["table"], meta["pos"], b.block_size)
+        for t, out in zip(layers, outs):
+            pkv.paged_kv_write(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], slots)
+            pkv.paged_decode_attention(None, t["q"], t["k_cache"], t["v_cache"], meta["table"],
+                                       meta["ctx"], scale, P, mp, ml, es, to)
+            pkv.paged_attention_reduce(out, ml, es, to, meta["ctx"], P)
+
+    step()                      # eager (also fills the library's per-device caches)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    for l, (o, th) in enumerate(zip(eager, pre)):
+        k, v, _ = oracle_pools_after_write(b, th)
+        e = max_err(o.cpu(), oracle_attention(b, th["q"], k, v))
+        print(f"  eager layer {l}: max abs err {e:.3e}", flush=True)
+        assert e <= TOL
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(4):
+        for o in outs:          # eager work between replays
+            o.fill_(float("nan"))
+        ml.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l, (o, want) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, want), (r, l)
+        print(f"  replay {r}: equal to eager", flush=True)
