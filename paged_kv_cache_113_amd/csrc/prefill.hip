@@ -418,6 +418,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
   auto stage_math = [&](auto ng, bool masked, int ok, int stage0, const PKV_LDS char* kb_,
                         const PKV_LDS char* vb_) {
     constexpr int NG = decltype(ng)::value;
+    // The matrix-core bursts run at raised wave priority: the other wave on
+    // the SIMD then issues its softmax in their gaps (3.5 % faster on the
+    // mixed step's chunks).
+    __builtin_amdgcn_s_setprio(1);
     f32x4 S[NG][kSub];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -437,6 +441,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
       }
     }
     uint4 p_hi[NG][2], p_lo[NG][2];
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       float s16[16];
@@ -489,6 +494,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
     // V^T operands of the 8 dim blocks: lane (d = col, group j) takes
     // positions 4j..4j+3 of each 16-row block (the same k order as P);
     // shared by the groups
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const PKV_LDS char* vbase = vb_ + 32 * h * (kD * 2);
@@ -508,6 +514,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // 3. the range, one stage at a time, two LDS buffers: wait for this
