@@ -421,8 +421,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sequences and KV heads shard with no communication; see DESIGN.md)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(sequences and KV heads shard across GPUs with no communication)",
               file=sys.stderr)
         sys.exit(2)
 
