@@ -572,6 +572,17 @@ def main():
             torch.cuda.synchronize()
             total_s += s0.elapsed_time(s1) / 1e3
     ms_per_step = total_s / args.steps * 1e3
+    warm_ms = None
+    if flush is not None:
+        # secondary figure: the same steps back to back, caches left warm
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        w0.record()
+        for _ in range(args.steps):
+            run_step()
+        w1.record()
+        torch.cuda.synchronize()
+        warm_ms = w0.elapsed_time(w1) / args.steps
     # the smaller kernels' own durations, from one more (untimed) step
     step(("write", "reduce"))
     torch.cuda.synchronize()
@@ -649,6 +660,9 @@ def main():
                                    "frac": round(flops / (dec_ms / 1e3) / 2.5e15, 4)}},
         "cpu_baseline": cpu,
     }
+    if warm_ms is not None:
+        line["warm_back_to_back"] = {"ms_per_step": round(warm_ms, 4),
+                                     "gbs": round(step_bytes / (warm_ms / 1e3) / 1e9, 2)}
     print(json.dumps(line), flush=True)
 
 
