@@ -398,7 +398,8 @@ def cpu_baseline(batch, th, target_s: float, threads: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 10 for the 32-layer decode step, 20 otherwise)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode_step_bf16",
                     choices=["decode_step_bf16", "mha_fp16", "gqa_shared_bf16",
@@ -418,6 +419,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 10 if args.workload == "decode_step_bf16" else 20
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -583,16 +586,17 @@ def main():
         w1.record()
         torch.cuda.synchronize()
         warm_ms = w0.elapsed_time(w1) / args.steps
-    # the smaller kernels' own durations, from one more (untimed) step
-    step(("write", "reduce"))
+    # the smaller kernels' own durations, from untimed steps (at least 10 calls)
+    for _ in range(max(1, -(-10 // L))):
+        step(("write", "reduce"))
     torch.cuda.synchronize()
 
     def avg_ms(name):
         xs = [a.elapsed_time(b) for a, b in ev[name]]
-        return (float(np.mean(xs)), float(np.percentile(xs, 10)), float(np.percentile(xs, 90))) \
-            if xs else (0.0, 0.0, 0.0)
+        return (float(np.mean(xs)), float(np.percentile(xs, 10)), float(np.percentile(xs, 90)),
+                float(np.median(xs))) if xs else (0.0, 0.0, 0.0, 0.0)
 
-    dec_ms, dec_p10, dec_p90 = avg_ms("decode")
+    dec_ms, dec_p10, dec_p90, dec_med = avg_ms("decode")
     red_ms = avg_ms("reduce")[0]
     wr_ms = avg_ms("write")[0]
     logical_bytes = kv_bytes(batch, batch.context_lens)
@@ -643,7 +647,8 @@ def main():
         if varlen else None,
         "new_tokens_per_s": round(batch.num_seqs / (ms_per_step / 1e3), 1)
         if batch.positions is not None else None,
-        "kernels_ms": {"decode_avg": round(dec_ms, 4), "decode_p10": round(dec_p10, 4),
+        "kernels_ms": {"decode_avg": round(dec_ms, 4), "decode_median": round(dec_med, 4),
+                       "decode_p10": round(dec_p10, 4),
                        "decode_p90": round(dec_p90, 4), "reduce_avg": round(red_ms, 4),
                        "write_avg": round(wr_ms, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
