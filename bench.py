@@ -74,6 +74,37 @@ def traffic_for(workload: str, kernel: str = "decode_split", sources=DECODE_SOUR
     return rec.get("hbm_bytes_per_launch")
 
 
+def read_ceiling(dev, reps: int = 5):
+    """Measured streaming-read ceiling of this device for the split decode
+    kernel's stream shape (the library's read probe: 8 KiB tiles, 4 KiB from
+    each of two 2 GiB buffers, in a seeded shuffled order, non-temporal
+    16-byte loads, each wave reading a contiguous run): median GB/s."""
+    import torch
+    import paged_kv_cache_113_amd as pkv
+    tiles = 1 << 19
+    a = torch.empty(tiles * 4096, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.fill_(2)
+    order = torch.from_numpy(
+        np.random.default_rng(7).permutation(tiles).astype(np.int32)).to(dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        pkv.stream_read_probe(a, b, order, sink)
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pkv.stream_read_probe(a, b, order, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a, b, order, sink
+    torch.cuda.empty_cache()
+    return 2.0 * 4096 * tiles / (float(np.median(ts)) / 1e3) / 1e9
+
+
 def kv_bytes(batch, lens) -> float:
     e = {"f32": 4, "f16": 2, "bf16": 2}[batch.dtype]
     return float(np.sum(lens, dtype=np.int64)) * 2 * batch.num_kv_heads * batch.head_size * e
@@ -416,6 +447,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured in a HIP graph (per-kernel times "
                          "still come from eager steps)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling probe")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -616,6 +649,8 @@ def main():
     pairs = float(visible_pairs(batch).sum()) if varlen else positions
     flops = 4.0 * batch.num_heads * batch.head_size * pairs   # q.K and P.V, per layer
 
+    ceiling = None if args.no_ceiling else read_ceiling(dev)
+
     cpu = None
     if cpu_host is not None:
         threads = min(os.cpu_count() or 1, 16)
@@ -659,6 +694,12 @@ def main():
                      else "decode_split_kernel" if P > 0 else "decode_whole_kernel",
                      "bytes_per_launch": layer_bytes,
                      "logical_bytes_per_launch": logical_bytes,
+                     "measured_ceiling": None if ceiling is None else {
+                         "gbs": round(ceiling, 2), "frac": round(achieved / ceiling, 4),
+                         "probe": "pkv_stream_read_probe: 8 KiB tiles (4 KiB from each of two "
+                                  "2 GiB buffers) in a seeded shuffled order, non-temporal "
+                                  "16-byte loads, one 4-wave workgroup per CU, each wave "
+                                  "reading a contiguous run with two tiles in flight"},
                      "mfma_view": {"flops_per_launch": flops,
                                    "achieved_tflops": round(flops / (dec_ms / 1e3) / 1e12, 2),
                                    "peak_tflops": 2500.0,

@@ -410,6 +410,30 @@ int pkv_pool_cache_full_blocks(pkv_block_pool* pool, const int32_t* table,
 int pkv_pool_state(const pkv_block_pool* pool, int32_t* ref_out, int32_t* free_out,
                    uint8_t* cached_out);
 
+/*
+ * pkv_stream_read_probe -- a measurement aid, not part of the attention path:
+ * the read bandwidth that a read-once stream shaped like the split decode
+ * kernel's K/V stream reaches on the current device (the measured ceiling
+ * that its rates are compared with, beside the datasheet peak).
+ *
+ * Reads, for each i < num_tiles, the 4096-byte tile tile_order[i] of a and
+ * the tile of b at the same index (8 KiB per i: a K and a V tile); the waves
+ * of one 4-wave workgroup per CU each read a contiguous run of the order with
+ * two tiles in flight, in 16-byte loads with the non-temporal hint, as the
+ * split decode kernel does. a and b: device buffers of buffer_bytes each (a
+ * multiple of 4096); tile_order: device int32 [num_tiles] (an index outside
+ * [0, buffer_bytes / 4096) reads tile 0; a wave given a single tile reads it
+ * twice); sink: 16 bytes of device memory,
+ * written only on a data-dependent condition that keeps the loads (its
+ * contents mean nothing). The caller owns every buffer and times the call on
+ * its stream: bytes read = 8192 * num_tiles.
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_LAUNCH. num_tiles == 0 is a
+ * no-op.
+ */
+int pkv_stream_read_probe(const void* a, const void* b, int64_t buffer_bytes,
+                          const int32_t* tile_order, int64_t num_tiles, void* sink,
+                          void* stream);
+
 /* pkv_strerror -- static description of a pkv_status code. */
 const char* pkv_strerror(int code);
 

@@ -51,6 +51,7 @@ SIGNATURES = {
     "pkv_pool_admit": (_I32, [_P, _P, _I64, _P, _I64, _P, _P]),
     "pkv_pool_cache_full_blocks": (_I32, [_P, _P, _P, _I64, _P, _I64]),
     "pkv_pool_state": (_I32, [_P, _P, _P, _P]),
+    "pkv_stream_read_probe": (_I32, [_P, _P, _I64, _P, _I64, _P, _P]),
     "pkv_strerror": (ctypes.c_char_p, [_I32]),
 }
 
@@ -353,6 +354,19 @@ class BlockPool:
         n = lib.pkv_pool_state(self._h, ref, free, cached)
         _check("pkv_pool_state", n if n < 0 else 0)
         return list(ref), list(free[:n]), [bool(c) for c in cached]
+
+
+def stream_read_probe(a, b, tile_order, sink, stream=None):
+    """Read tile tile_order[i] (4 KiB) of a and of b for every i, in the split
+    decode kernel's stream shape: a measurement aid (bytes read = 8192 *
+    len(tile_order)); the caller times the call."""
+    _dev(a, b, tile_order, sink)
+    assert tile_order.dtype == torch.int32 and sink.numel() * sink.element_size() >= 16
+    nbytes = a.numel() * a.element_size()
+    assert b.numel() * b.element_size() == nbytes
+    _check("pkv_stream_read_probe", lib.pkv_stream_read_probe(
+        _ptr(a), _ptr(b), nbytes, _ptr(tile_order), tile_order.numel(), _ptr(sink),
+        _stream(stream)))
 
 
 def pkv_strerror(code):

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 SOURCES = ["api.cpp", "cache_ops.hip", "decode_fast.hip", "decode_generic.hip", "block_ops.hip",
-           "prefill.hip", "prefix_cache.cpp"]
+           "prefill.hip", "prefix_cache.cpp", "stream_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -287,6 +287,16 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v
                                              eb, as_stream(stream)));
 }
 
+int pkv_stream_read_probe(const void* a, const void* b, int64_t buffer_bytes,
+                          const int32_t* tile_order, int64_t num_tiles, void* sink,
+                          void* stream) {
+  if (buffer_bytes < 4096 || buffer_bytes % 4096 != 0 || num_tiles < 0) return PKV_ERR_SHAPE;
+  if (num_tiles == 0) return PKV_OK;
+  if (!a || !b || !tile_order || !sink) return PKV_ERR_NULL;
+  return launch_status(pkv::launch_stream_probe(a, b, buffer_bytes, tile_order, num_tiles, sink,
+                                                as_stream(stream)));
+}
+
 const char* pkv_strerror(int code) {
   switch (code) {
     case PKV_OK: return "ok";

@@ -204,3 +204,14 @@ def test_product_path_does_not_import_the_oracle():
                     text = open(os.path.join(dirpath, fn)).read()
                     assert "import oracle" not in text and "from oracle" not in text, fn
                     assert "attn_ref" not in text and "liboracle" not in text, fn
+
+
+def test_stream_probe_validation(lib):
+    f = lib.pkv_stream_read_probe
+    assert f(P, P, 4095, P, 8, P, None) == ESHAPE      # not whole 4 KiB tiles
+    assert f(P, P, 0, P, 8, P, None) == ESHAPE
+    assert f(P, P, 8192, P, -1, P, None) == ESHAPE
+    assert f(P, P, 8192, P, 0, P, None) == OK          # nothing to read
+    assert f(None, P, 8192, P, 8, P, None) == ENULL
+    assert f(P, P, 8192, None, 8, P, None) == ENULL
+    assert f(P, P, 8192, P, 8, None, None) == ENULL
