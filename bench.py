@@ -74,20 +74,23 @@ def traffic_for(workload: str, kernel: str = "decode_split", sources=DECODE_SOUR
     return rec.get("hbm_bytes_per_launch")
 
 
-def read_ceiling(dev, reps: int = 5):
+def read_ceiling(dev, nbytes: float = 0.0, reps: int = 5):
     """Measured streaming-read ceiling of this device for the split decode
     kernel's stream shape (the library's read probe: 8 KiB tiles, 4 KiB from
-    each of two 2 GiB buffers, in a seeded shuffled order, non-temporal
-    16-byte loads, each wave reading a contiguous run): median GB/s."""
+    each of two buffers of at least 2 GiB, distinct tiles in a seeded shuffled
+    order, non-temporal 16-byte loads, each wave reading a contiguous run),
+    over nbytes (the kernel's own bytes per launch; 4 GiB if 0): median GB/s.
+    A short stream pays the same start and drain as a short kernel."""
     import torch
     import paged_kv_cache_113_amd as pkv
-    tiles = 1 << 19
+    n = int(nbytes // 8192) if nbytes > 0 else 1 << 19
+    tiles = max(n, 1 << 19)
     a = torch.empty(tiles * 4096, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
     a.fill_(1)
     b.fill_(2)
     order = torch.from_numpy(
-        np.random.default_rng(7).permutation(tiles).astype(np.int32)).to(dev)
+        np.random.default_rng(7).permutation(tiles)[:n].astype(np.int32)).to(dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     for _ in range(2):
         pkv.stream_read_probe(a, b, order, sink)
@@ -102,7 +105,7 @@ def read_ceiling(dev, reps: int = 5):
         ts.append(e0.elapsed_time(e1))
     del a, b, order, sink
     torch.cuda.empty_cache()
-    return 2.0 * 4096 * tiles / (float(np.median(ts)) / 1e3) / 1e9
+    return 8192.0 * n / (float(np.median(ts)) / 1e3) / 1e9
 
 
 def kv_bytes(batch, lens) -> float:
@@ -649,7 +652,7 @@ def main():
     pairs = float(visible_pairs(batch).sum()) if varlen else positions
     flops = 4.0 * batch.num_heads * batch.head_size * pairs   # q.K and P.V, per layer
 
-    ceiling = None if args.no_ceiling else read_ceiling(dev)
+    ceiling = None if args.no_ceiling else read_ceiling(dev, layer_bytes)
 
     cpu = None
     if cpu_host is not None:
@@ -696,10 +699,11 @@ def main():
                      "logical_bytes_per_launch": logical_bytes,
                      "measured_ceiling": None if ceiling is None else {
                          "gbs": round(ceiling, 2), "frac": round(achieved / ceiling, 4),
-                         "probe": "pkv_stream_read_probe: 8 KiB tiles (4 KiB from each of two "
-                                  "2 GiB buffers) in a seeded shuffled order, non-temporal "
-                                  "16-byte loads, one 4-wave workgroup per CU, each wave "
-                                  "reading a contiguous run with two tiles in flight"},
+                         "probe": "pkv_stream_read_probe over the kernel's bytes per launch: "
+                                  "distinct 8 KiB tiles (4 KiB from each of two buffers of "
+                                  ">= 2 GiB) in a seeded shuffled order, non-temporal 16-byte "
+                                  "loads, one 4-wave workgroup per CU, each wave reading a "
+                                  "contiguous run with two tiles in flight"},
                      "mfma_view": {"flops_per_launch": flops,
                                    "achieved_tflops": round(flops / (dec_ms / 1e3) / 1e12, 2),
                                    "peak_tflops": 2500.0,
