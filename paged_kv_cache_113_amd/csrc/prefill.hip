@@ -305,25 +305,61 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
   // of a transposed read.
   auto kbuf = [&](int par) { return (PKV_LDS char*)(s_dyn) + par * (2 * kStageBytes); };
   auto vbuf = [&](int par) { return (PKV_LDS char*)(s_dyn) + par * (2 * kStageBytes) + kStageBytes; };
+  // The table entries of a stage. A power-of-two block size (the usual case)
+  // turns the position -> entry division into a shift, and the at most four
+  // consecutive entries the stage touches come in one scalar load (plus one
+  // for the entry of this wave's 16-row block): this scalar work sits on
+  // every stage's path. Entries are int32, so one unsigned compare against
+  // min(num_blocks, 2^31 - 1) checks 0 <= entry < num_blocks.
+  const int bsh = (a.block_size & (a.block_size - 1)) == 0 ? __builtin_ctz(a.block_size) : -1;
+  const uint32_t nb32 = a.num_blocks < 0x7fffffff ? static_cast<uint32_t>(a.num_blocks)
+                                                  : 0x7fffffffu;
+  // Validity bits of the stage's four 16-row blocks (bit m: the block has a
+  // table entry in the pool; if not, block 0 is read instead and its rows
+  // are masked), the entry of block w and the offset of its first row inside
+  // its block.
+  auto stage_blocks = [&](const PfCursor& c, int& ok, int64_t& bw, int& in_block) {
+    const int32_t* row = row_of(c.s);
+    const int t0 = c.t * kStage;
+    const int tw = t0 + w * kTile;
+    if (bsh >= 0 && (t0 >> bsh) + 3 < a.max_blocks) {
+      // t0 is a multiple of 64: of B too when B <= 64, and a larger block
+      // holds the whole stage; so block m is entry (t0 >> log2 B) + (16 m >> log2 B)
+      typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+      const i32x4 e = read_only(reinterpret_cast<const i32x4*>(row + (t0 >> bsh)));
+      const int vb = (static_cast<uint32_t>(e.x) < nb32) | (static_cast<uint32_t>(e.y) < nb32) << 1 |
+                     (static_cast<uint32_t>(e.z) < nb32) << 2 |
+                     (static_cast<uint32_t>(e.w) < nb32) << 3;
+      ok = 0;
+#pragma unroll
+      for (int m = 0; m < kSub; ++m) ok |= ((vb >> ((m * kTile) >> bsh)) & 1) << m;
+      const int32_t ew = read_only(row + (tw >> bsh));
+      bw = static_cast<uint32_t>(ew) < nb32 ? ew : -1;
+      in_block = tw & (a.block_size - 1);
+      return;
+    }
+    ok = 0;
+    bw = -1;
+#pragma unroll
+    for (int m = 0; m < kSub; ++m) {
+      const int64_t b = physical_block(row, t0 + m * kTile, a.block_size, a.max_blocks,
+                                       a.num_blocks);
+      ok |= (b >= 0) << m;
+      if (m == w) bw = b;
+    }
+    in_block = tw % a.block_size;
+  };
   // In-LDS loads of a stage into buffer par: wave w fills 16-row block w of
   // the stage (K and V, four 1 KiB load instructions each); lane l of
   // instruction j writes chunk l % 16 of block row 4j + l / 16, so it loads
   // the global chunk the row's swizzle puts there. Returns the blocks'
-  // validity bits (bit m: block m has a table entry in the pool; if not,
-  // block 0 is read instead and its rows are masked).
+  // validity bits.
   auto dma_stage = [&](const PfCursor& c, int par) {
-    int ok = 0;
-    int64_t mine = 0;
-#pragma unroll
-    for (int m = 0; m < kSub; ++m) {
-      const int tok0 = c.t * kStage + m * kTile;
-      const int64_t blk = physical_block(row_of(c.s), tok0, a.block_size, a.max_blocks,
-                                         a.num_blocks);
-      ok |= (blk >= 0) << m;
-      if (m == w)
-        mine = (blk < 0 ? 0 : blk) * block_stride + kvh * head_stride +
-               static_cast<int64_t>(tok0 % a.block_size) * kD * 2;
-    }
+    int ok, in_block;
+    int64_t bw;
+    stage_blocks(c, ok, bw, in_block);
+    const int64_t mine = (bw < 0 ? 0 : bw) * block_stride + kvh * head_stride +
+                         static_cast<int64_t>(in_block) * kD * 2;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 4 * j + (lane >> 4);  // row within block w

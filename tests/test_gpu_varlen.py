@@ -51,6 +51,8 @@ SMALL = {
     "bf16_g8_b16": lambda: _mix("bf16_g8_b16", "bf16", 16, 2, 128, 16, 203),
     "f16_g16_b64": lambda: _mix("f16_g16_b64", "f16", 32, 2, 128, 64, 204),
     "bf16_g3_b16": lambda: _mix("bf16_g3_b16", "bf16", 12, 4, 128, 16, 205),
+    # a block size that is a multiple of 16 but not a power of two
+    "bf16_g4_b48": lambda: _mix("bf16_g4_b48", "bf16", 32, 8, 128, 48, 210),
     "f32_d8_b4": lambda: _mix("f32_d8_b4", "f32", 4, 2, 8, 4, 206, hmax=40),
     "bf16_d64_b8": lambda: _mix("bf16_d64_b8", "bf16", 8, 2, 64, 8, 207, hmax=100),
     # MHA: chunks of 128+ tokens reach the prefill kernel (one head per KV head)
