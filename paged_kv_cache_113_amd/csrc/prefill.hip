@@ -305,6 +305,17 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
   // of a transposed read.
   auto kbuf = [&](int par) { return (PKV_LDS char*)(s_dyn) + par * (2 * kStageBytes); };
   auto vbuf = [&](int par) { return (PKV_LDS char*)(s_dyn) + par * (2 * kStageBytes) + kStageBytes; };
+  // The lane's byte offsets inside its 16-row block for the in-LDS loads:
+  // instruction j, row r = 4 j + l / 16, the global chunk that the row's
+  // swizzle keeps at LDS chunk l % 16.
+  uint32_t kdo[4], vdo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    const int cs = lane & 15;
+    kdo[j] = static_cast<uint32_t>(r * kD * 2 + ((cs ^ r) << 4));
+    vdo[j] = static_cast<uint32_t>(r * kD * 2 + ((cs ^ ((r & 7) << 1)) << 4));
+  }
   // The table entries of a stage. A power-of-two block size (the usual case)
   // turns the position -> entry division into a shift, and the at most four
   // consecutive entries the stage touches come in one scalar load (plus one
@@ -318,7 +329,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
   // table entry in the pool; if not, block 0 is read instead and its rows
   // are masked), the entry of block w and the offset of its first row inside
   // its block.
-  auto stage_blocks = [&](const PfCursor& c, int& ok, int64_t& bw, int& in_block) {
+  auto stage_blocks = [&](const PfCursor& c, int& ok, int32_t& bw, int& in_block) {
     const int32_t* row = row_of(c.s);
     const int t0 = c.t * kStage;
     const int tw = t0 + w * kTile;
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
       const int64_t b = physical_block(row, t0 + m * kTile, a.block_size, a.max_blocks,
                                        a.num_blocks);
       ok |= (b >= 0) << m;
-      if (m == w) bw = b;
+      if (m == w) bw = static_cast<int32_t>(b);  // a valid id is an int32 entry
     }
     in_block = tw % a.block_size;
   };
@@ -356,20 +367,19 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
   // validity bits.
   auto dma_stage = [&](const PfCursor& c, int par) {
     int ok, in_block;
-    int64_t bw;
+    int32_t bw;
     stage_blocks(c, ok, bw, in_block);
-    const int64_t mine = (bw < 0 ? 0 : bw) * block_stride + kvh * head_stride +
-                         static_cast<int64_t>(in_block) * kD * 2;
+    const int64_t mine = static_cast<int64_t>(bw < 0 ? 0 : bw) * block_stride +
+                         kvh * head_stride + static_cast<int64_t>(in_block) * kD * 2;
+    // a wave-uniform base plus the lane's fixed 32-bit offset: one add per
+    // load, no per-lane offset arithmetic
+    const char* kg = kc + mine;
+    const char* vg = vc + mine;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = 4 * j + (lane >> 4);  // row within block w
-      const int cs = lane & 15;
-      const int64_t roff = mine + static_cast<int64_t>(r) * kD * 2;
       const int at = (kTile * w + 4 * j) * kD * 2;
-      __builtin_amdgcn_global_load_lds(kc + roff + ((cs ^ r) << 4),
-                                       (PKV_LDS void*)(kbuf(par) + at), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vc + roff + ((cs ^ ((r & 7) << 1)) << 4),
-                                       (PKV_LDS void*)(vbuf(par) + at), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kg + kdo[j], (PKV_LDS void*)(kbuf(par) + at), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vg + vdo[j], (PKV_LDS void*)(vbuf(par) + at), 16, 0, 0);
     }
     return ok;
   };
