@@ -481,9 +481,14 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   // the same stores issued in one burst at the end of the range do not. A
   // unit's last piece also marks its remaining slots unused (l = 0) so the
   // merge skips them. Live columns are a prefix [0, nl) of the 16 columns.
+  // With multi-token queries a unit done in a single piece writes its output
+  // rows themselves, and l = -1 into their first slot, so the merge leaves
+  // them alone (decode calls keep the output untouched, as their contract
+  // says).
   //
   // Record: int4 header {sequence (decode) or first query row, column group,
-  // slot, nl | mark << 16}, then nl rows of 128 floats, then nl (m, l) pairs.
+  // slot, nl | mark << 16 | single << 17}, then nl rows of 128 floats, then
+  // nl (m, l) pairs.
   PKV_LDS char* stage = (PKV_LDS char*)(s_pre) +
                         ((static_cast<int>(sizeof(int)) * (S + 1) + 15) & ~15) + w * stage_bytes;
   int st_used = 0, st_n = 0;  // bytes and records staged (wave-uniform)
@@ -522,25 +527,31 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
       const int cg = __builtin_amdgcn_readfirstlane(static_cast<int>(h[1]));
       const int pc = __builtin_amdgcn_readfirstlane(static_cast<int>(h[2]));
       const int nl = __builtin_amdgcn_readfirstlane(static_cast<int>(h[3] & 0xffffu));
-      const int mark = __builtin_amdgcn_readfirstlane(static_cast<int>(h[3] >> 16));
+      const int mark = __builtin_amdgcn_readfirstlane(static_cast<int>((h[3] >> 16) & 1u));
+      const int single = __builtin_amdgcn_readfirstlane(static_cast<int>(h[3] >> 17));
       if (pc < mp) {
         for (int r0 = 0; r0 < nl; r0 += 2) {
           const int r = r0 + (lane >> 5);
           const int ch = lane & 31;
           if (r < nl) {
             const f32x4 v = *(const PKV_LDS f32x4*)(rec + 16 + r * (kD * 4) + ch * 16);
-            store_untracked(a.tmp_out + (row_index(sq, cg, r) * mp + pc) * kD + ch * 4,
-                            make_float4(v[0], v[1], v[2], v[3]));
+            float* dst = single ? a.out + row_index(sq, cg, r) * kD
+                                : a.tmp_out + (row_index(sq, cg, r) * mp + pc) * kD;
+            store_untracked(dst + ch * 4, make_float4(v[0], v[1], v[2], v[3]));
           }
         }
         if (lane < nl) {
           const f32x2 ml = *(const PKV_LDS f32x2*)(rec + 16 + nl * (kD * 4) + lane * 8);
           const int64_t e = row_index(sq, cg, lane) * mp + pc;
-          store_untracked(a.max_logits + e, ml[0]);
-          store_untracked(a.exp_sums + e, ml[1]);
+          if (single) {
+            store_untracked(a.exp_sums + e, -1.f);
+          } else {
+            store_untracked(a.max_logits + e, ml[0]);
+            store_untracked(a.exp_sums + e, ml[1]);
+          }
         }
       }
-      if (mark) mark_rest(sq, cg, pc, nl);
+      if (mark && !single) mark_rest(sq, cg, pc, nl);
       off += rec_bytes(nl);
     }
     st_used = 0;
@@ -553,6 +564,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     const int sq = kVar ? c.q0 : c.s;
     const int cg = kVar ? c.c : 0;
     const bool last = c.t == c.n - 1;
+    const bool single = kVar && last && piece == 0;
     const int need = rec_bytes(nl);
     if (st_used + need > stage_bytes) flush();
     if (need <= stage_bytes) {
@@ -567,13 +579,16 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
       if (lane == 0)
         *(PKV_LDS u32x4*)(rec) = u32x4{static_cast<unsigned>(sq), static_cast<unsigned>(cg),
                                        static_cast<unsigned>(piece),
-                                       static_cast<unsigned>(nl | (last << 16))};
+                                       static_cast<unsigned>(nl | (last << 16) |
+                                                             (single << 17))};
       st_used += need;
       ++st_n;
     } else {
       // no room even in an empty area: write directly
       if (col < nl && piece < mp) {
-        float* dst = a.tmp_out + (row_index(sq, cg, col) * mp + piece) * kD + 4 * grp;
+        float* dst = (single ? a.out + row_index(sq, cg, col) * kD
+                             : a.tmp_out + (row_index(sq, cg, col) * mp + piece) * kD) +
+                     4 * grp;
 #pragma unroll
         for (int db = 0; db < 8; ++db)
           store_untracked(dst + 16 * db,
@@ -581,11 +596,15 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
                                       st.acc[db][2] * inv, st.acc[db][3] * inv));
         if (grp == 0) {
           const int64_t e = row_index(sq, cg, col) * mp + piece;
-          store_untracked(a.max_logits + e, st.m_run * kLn2);
-          store_untracked(a.exp_sums + e, l_col);
+          if (single) {
+            store_untracked(a.exp_sums + e, -1.f);
+          } else {
+            store_untracked(a.max_logits + e, st.m_run * kLn2);
+            store_untracked(a.exp_sums + e, l_col);
+          }
         }
       }
-      if (last) mark_rest(sq, cg, piece, nl);
+      if (last && !single) mark_rest(sq, cg, piece, nl);
     }
     st.reset();
     piece = 0;

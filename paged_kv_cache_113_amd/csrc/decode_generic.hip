@@ -200,12 +200,15 @@ __global__ __launch_bounds__(kRedWaves * 64) void reduce_kernel(
   const int seq = static_cast<int>(orow / num_heads);
   const int D = head_size;
   const int mp = max_partitions;
-  // without lengths every row takes part (multi-token queries: every query
-  // row's pieces are written, unused ones with l = 0)
-  const int n = !active ? 0
-                : (context_lens == nullptr || read_only(context_lens + seq) > 0) ? mp : 0;
   const float* __restrict__ m = max_logits + orow * mp;
   const float* __restrict__ l = exp_sums + orow * mp;
+  // without lengths every row takes part (multi-token queries: every query
+  // row's pieces are written, unused ones with l = 0), except a row whose
+  // work was a single piece: that piece wrote the output itself and marked
+  // its first slot with l = -1
+  const bool done = active && context_lens == nullptr && l[0] < 0.f;
+  const int n = !active || done ? 0
+                : (context_lens == nullptr || read_only(context_lens + seq) > 0) ? mp : 0;
   const float* __restrict__ o = tmp_out + orow * mp * D;
 
   float mx = -INFINITY;
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(kRedWaves * 64) void reduce_kernel(
     }
   }
   den = unit_sum(den);
-  if (!active) return;
+  if (!active || done) return;
   const bool any = n > 0 && den > 0.f;
   float* __restrict__ dst = out + orow * D;
   if constexpr (kVec) {
@@ -310,6 +313,9 @@ __global__ __launch_bounds__(kRedWaves * 64) void reduce_row_kernel(
   const int n = (context_lens == nullptr || read_only(context_lens + seq) > 0) ? mp : 0;
   const float* __restrict__ m = max_logits + row * mp;
   const float* __restrict__ l = exp_sums + row * mp;
+  // multi-token queries: a row done in a single piece (l = -1 in its first
+  // slot) already holds its output (the whole wave)
+  if (context_lens == nullptr && l[0] < 0.f) return;
   const float* __restrict__ o = tmp_out + row * mp * D;
 
   float mx = -INFINITY;

@@ -419,14 +419,26 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
 #pragma unroll
   for (int gi = 0; gi < kGroupsPerWave; ++gi) st[gi].reset();
 
+  // A unit done in a single piece writes its output rows itself and l = -1
+  // into their first slot, which tells the merge to leave them alone.
   auto finish = [&](const PfCursor& c) {
+    const bool single = piece == 0 && c.t == c.n - 1;
 #pragma unroll
     for (int gi = 0; gi < kGroupsPerWave; ++gi) {
       const float l_col = st[gi].column_sum();
       if (live(c, gi)) {
         const int64_t prow = static_cast<int64_t>(c.q0 + token_of(c, gi)) * a.num_heads +
                              kvh * G + my_head;
-        if (piece < mp) {
+        if (single) {
+          const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
+          float* dst = a.out + prow * kD + 4 * grp;
+#pragma unroll
+          for (int db = 0; db < 8; ++db)
+            *reinterpret_cast<float4*>(dst + 16 * db) =
+                make_float4(st[gi].acc[db][0] * inv, st[gi].acc[db][1] * inv,
+                            st[gi].acc[db][2] * inv, st[gi].acc[db][3] * inv);
+          if (grp == 0) a.exp_sums[prow * mp] = -1.f;
+        } else if (piece < mp) {
           const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
           float* dst = a.tmp_out + (prow * mp + piece) * kD + 4 * grp;
 #pragma unroll
@@ -439,7 +451,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
             a.exp_sums[prow * mp + piece] = l_col;
           }
         }
-        if (c.t == c.n - 1 && grp == 0) {
+        if (!single && c.t == c.n - 1 && grp == 0) {
           for (int p = piece + 1; p < mp; ++p) {
             a.max_logits[prow * mp + p] = -INFINITY;
             a.exp_sums[prow * mp + p] = 0.f;
