@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
   // instruction j writes chunk l % 16 of block row 4j + l / 16, so it loads
   // the global chunk the row's swizzle puts there. Returns the blocks'
   // validity bits.
-  auto dma_stage = [&](const PfCursor& c, int par) {
+  auto dma_stage = [&](const PfCursor& c, PKV_LDS char* kd, PKV_LDS char* vd) {
     int ok, in_block;
     int32_t bw;
     stage_blocks(c, ok, bw, in_block);
@@ -378,8 +378,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int at = (kTile * w + 4 * j) * kD * 2;
-      __builtin_amdgcn_global_load_lds(kg + kdo[j], (PKV_LDS void*)(kbuf(par) + at), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vg + vdo[j], (PKV_LDS void*)(vbuf(par) + at), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kg + kdo[j], (PKV_LDS void*)(kd + at), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vg + vdo[j], (PKV_LDS void*)(vd + at), 16, 0, 0);
     }
     return ok;
   };
@@ -582,31 +582,28 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
   //    math), then the math. V rows past what the unit sees, and rows of a
   //    block with no table entry, are zeroed first (one more barrier): P is 0
   //    there, and 0 * NaN would still be NaN.
-  load_q_unit(cur);
-  int okb = dma_stage(cur, 0);
-  for (int i = 0; i < len; ++i) {
-    const int par = i & 1;
-    wait_all_loads();
-    __syncthreads();
-    const int ok_now = okb;
-    const bool more = i + 1 < len;
-    PfCursor nx = cur;
-    if (more) {
-      nx = advance(cur);
-      okb = dma_stage(nx, par ^ 1);
-    }
-    {
-      const int vl = vlimit(cur);
-      if (vl < kStage || ok_now != (1 << kSub) - 1) {
+  //    The next stage's loads and this stage's math go through restrict
+  //    pointers of one function, so the compiler knows the in-LDS loads
+  //    write the other buffer and does not make this stage's LDS reads wait
+  //    for them.
+  using Two = std::integral_constant<int, 2>;
+  using One = std::integral_constant<int, 1>;
+  auto stage_step = [&](PKV_LDS char* __restrict__ kd, PKV_LDS char* __restrict__ vd,
+                        PKV_LDS char* __restrict__ ks, PKV_LDS char* __restrict__ vs,
+                        const PfCursor& nx, bool more, int ok_now, int& okb) {
+    if (more) okb = dma_stage(nx, kd, vd);
+    const int vl = vlimit(cur);
+    if (vl < kStage || ok_now != (1 << kSub) - 1) {
 #pragma unroll
-        for (int m = 0; m < kSub; ++m) {
-          const int row = kTile * m + (tid >> 4);
-          if (row >= vl || !((ok_now >> m) & 1))
-            *(PKV_LDS u32x4v*)(vbuf(par) + row * (kD * 2) + (tid & 15) * 16) =
-                u32x4v{0u, 0u, 0u, 0u};
-        }
-        __syncthreads();
+      for (int m = 0; m < kSub; ++m) {
+        const int row = kTile * m + (tid >> 4);
+        if (row >= vl || !((ok_now >> m) & 1))
+          *(PKV_LDS u32x4v*)(vs + row * (kD * 2) + (tid & 15) * 16) = u32x4v{0u, 0u, 0u, 0u};
       }
+      // the zeros are LDS writes: wait for those only (not for the next
+      // stage's loads in flight), then meet the other waves
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
     }
     const int stage0 = cur.t * kStage;
     // the whole stage is visible to the wave's first token (the others see
@@ -614,16 +611,23 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
     const int first_tok = cur.u * utok + kGroupsPerWave * w * tpg;
     const bool interior = ok_now == (1 << kSub) - 1 &&
                           stage0 + kStage <= cur.ctx - cur.qn + first_tok + 1;
-    using Two = std::integral_constant<int, 2>;
-    using One = std::integral_constant<int, 1>;
-    const PKV_LDS char* kb_now = kbuf(par);
-    const PKV_LDS char* vb_now = vbuf(par);
     // groups are filled in order: the second has tokens only if the first does
     if (group_live(cur, 1)) {
-      stage_math(Two(), !interior, ok_now, stage0, kb_now, vb_now);
+      stage_math(Two(), !interior, ok_now, stage0, ks, vs);
     } else if (group_live(cur, 0)) {
-      stage_math(One(), true, ok_now, stage0, kb_now, vb_now);
+      stage_math(One(), true, ok_now, stage0, ks, vs);
     }
+  };
+  load_q_unit(cur);
+  int okb = dma_stage(cur, kbuf(0), vbuf(0));
+  for (int i = 0; i < len; ++i) {
+    const int par = i & 1;
+    wait_all_loads();
+    __syncthreads();
+    const int ok_now = okb;
+    const bool more = i + 1 < len;
+    const PfCursor nx = more ? advance(cur) : cur;
+    stage_step(kbuf(par ^ 1), vbuf(par ^ 1), kbuf(par), vbuf(par), nx, more, ok_now, okb);
     const bool unit_ends = cur.t + 1 >= cur.n;
     if (unit_ends || !more) finish(cur);
     if (more && unit_ends) {
