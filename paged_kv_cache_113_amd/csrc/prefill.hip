@@ -572,6 +572,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
         }
       }
     }
+    // software pipeline: the transposed reads of the next dim block are in
+    // flight while the matrix cores work on this one
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int k = 0; k < 15; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NG, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NG, 0);
     __builtin_amdgcn_s_setprio(0);
   };
 
