@@ -11,28 +11,31 @@
 //
 // It takes the sequences whose query tokens fill at least kPrefillCols
 // (token, head) columns per KV head. There q.K^T is a real dense contraction
-// and the cost is in the matrix cores and in re-reading K/V, so a workgroup
-// of 4 waves loads each 64-position stage of K and V once into LDS and all
-// 4 waves use it, each for 2 groups of 16 columns (128 columns per stage):
+// and the cost is in the matrix cores, the VALU softmax and re-reading K/V,
+// so a workgroup of 4 waves loads each 64-position stage of K and V once into
+// LDS and all 4 waves use it, each for 2 groups of 16 columns (128 columns
+// per stage):
 //  * unit = (sequence, 8 column groups of 16/G tokens x G heads); wave w owns
 //    groups 2w and 2w + 1 of the unit;
-//  * a stage's K rows sit in LDS at a 272 B pitch (the 16 rows of an
-//    A-operand read start 4 banks apart), its V rows at a 288 B pitch that
-//    ds_read_b64_tr_b16 turns into V^T; one LDS buffer, the next stage's
-//    global loads held in registers during this stage's math, two barriers
-//    per stage;
-//  * per 32 positions and group: scores of two 16-position blocks on
-//    v_mfma_f32_16x16x32 (lane (col n, group j) gets positions 4j..4j+3 of
-//    each block), one online-softmax step over those 8 positions, and P.V on
-//    v_mfma_f32_16x16x32 with k running over exactly those 8 positions per
-//    lane: the lane's own probabilities are the P^T operand (a 16-bit high
-//    part and the rounding of the remainder), and two transposed reads of the
-//    two 16-row halves give the V^T operand, shared by both groups. The
-//    accumulators are rescaled only when some column's running max moved;
+//  * a stage arrives by in-LDS loads (global_load_lds_dwordx4, 1 KiB per
+//    instruction) into one of two stage buffers while the other is computed;
+//    rows are unpadded and swizzled against bank conflicts (K row r keeps
+//    16-byte chunk c at c ^ (r % 16), V row r keeps 32-byte segment g at
+//    g ^ (r % 8)); one barrier per stage;
+//  * per stage and group: the scores of its 64 positions (four 16-row blocks
+//    on v_mfma_f32_16x16x32; lane (col n, group j) gets positions
+//    16b + 4j .. 16b + 4j + 3 of block b), one online-softmax step over the
+//    lane's 16 positions, and P.V on v_mfma_f32_16x16x32 over the two
+//    32-position halves with k running over exactly those positions: the
+//    lane's own probabilities are the P^T operand (a 16-bit high part and the
+//    rounding of the remainder), two transposed LDS reads give the V^T
+//    operand, shared by both groups. The accumulators are rescaled only when
+//    some column's running max moved by more than 2^8;
 //  * work split: for each KV head the stream of all units' stages is cut into
 //    equal ranges, one per workgroup (the decode kernel's balanced split at
 //    workgroup granularity); a range ends a piece wherever a unit or the
-//    range ends, and the reduce kernel merges the pieces.
+//    range ends, and the reduce kernel merges the pieces (a unit done in one
+//    piece writes its output rows itself).
 #include <atomic>
 #include <type_traits>
 
