@@ -203,10 +203,12 @@ int paged_attention_reduce(float* out, const float* max_logits, const float* exp
  * [num_tokens, num_heads, head_size] float32. The call writes `out` itself:
  * on the matrix-core path it splits each sequence's work over the whole GPU
  * into pieces (at most max_partitions per query row, so max_partitions >= 8
- * is a good choice; 1 serialises each KV head), writes their partials into
- * max_logits/exp_sums [num_tokens, num_heads, max_partitions] and tmp_out
- * [num_tokens, num_heads, max_partitions, head_size] float32 (size:
- * paged_attention_workspace_bytes(num_tokens, ...)), and merges them. The
+ * is a good choice; 1 serialises each KV head), keeps their partials in the
+ * workspace max_logits/exp_sums [num_tokens, num_heads, max_partitions] and
+ * tmp_out [num_tokens, num_heads, max_partitions, head_size] float32 (size:
+ * paged_attention_workspace_bytes(num_tokens, ...)) and merges them; rows
+ * done in a single piece are written directly. The workspace's contents
+ * afterwards are unspecified. The
  * matrix-core path covers the shapes of paged_decode_attention's fast path
  * with a finite scale > 0; the plain path (everything else) ignores the
  * workspace. Rows no sequence claims
