@@ -3,6 +3,8 @@
 Every expected value here is printed on the pages (tests/golden/*.json, each
 with its citation) or follows from a definition checked by brute force.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -213,3 +215,29 @@ def test_bench_block_utilisation_matches_oracle(make):
     assert bench.block_utilisation(b) == round(want["utilisation"], 4)
     if make == "tiny":
         assert (want["live_positions"], want["allocated_slots"]) == (13, 16)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more, it exits with status 2 and
+    says why, before touching a GPU."""
+    import subprocess
+    import sys
+    from conftest import ROOT
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_bench_traffic_lookup_follows_sources():
+    """The bench line's traffic figure comes from the committed counter
+    summary only while the kernel sources' hash matches it."""
+    import json
+    import bench
+    from conftest import ROOT
+    path = os.path.join(ROOT, "profiles", "decode_split_decode_step_bf16_traffic.json")
+    rec = json.load(open(path))
+    assert bench.traffic_for("decode_step_bf16") == (
+        rec["hbm_bytes_per_launch"]
+        if rec["kernel_source_sha256"] == bench.kernel_source_hash() else None)
+    assert bench.traffic_for("no_such_workload") is None
