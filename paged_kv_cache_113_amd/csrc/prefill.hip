@@ -96,6 +96,20 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
   }
 }
 
+// Maximum of two scores. The NaN-propagating form needs no quieting of its
+// inputs (the IEEE-mode fmaxf does, one extra instruction per matrix-core
+// result); no score that reaches it is NaN: positions a column must not see
+// are replaced by -inf first.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float vmax_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // 8 probabilities in k order as a 16x16x32 operand pair (high parts, remainders).
 template <typename T>
 __device__ __forceinline__ void split_p8(const float* p, uint4& hi, uint4& lo) {
@@ -525,10 +539,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_split_kernel(DecodeArgs a,
       // the max is taken on the raw scores: scaling by qk_scale > 0 keeps it
       float m8[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m8[i] = fmaxf(s16[i], s16[8 + i]);
-      float mt = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
-                       fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
-      mt = max_xor32(max_xor16(mt)) * qk_scale;
+      for (int i = 0; i < 8; ++i) m8[i] = vmax(s16[i], s16[8 + i]);
+      float mt = vmax(vmax(vmax(m8[0], m8[1]), vmax(m8[2], m8[3])),
+                      vmax(vmax(m8[4], m8[5]), vmax(m8[6], m8[7])));
+      mt = vmax_xor32(vmax_xor16(mt)) * qk_scale;
       const float m_old = st[gi].m_run;
       const bool move = mt > m_old + kLazyLog2;
       const float m_ref = move ? mt : m_old;
