@@ -58,136 +58,159 @@ def translate(table, position: int, block_size: int) -> int:
     return table[logical] * block_size + offset
 
 
+class _Seq:
+    """One request: the physical blocks of its logical blocks, in order, and
+    how many tokens it holds."""
+
+    __slots__ = ("blocks", "length")
+
+    def __init__(self, blocks, length: int):
+        self.blocks = blocks
+        self.length = length
+
+
 class BlockAllocator:
     """FIFO block allocator with per-block reference counts.
 
     Blocks are ints in [0, num_blocks). ``initial_free`` sets the order of the
-    free list (default: 0..N-1, as in the pages' timeline); a seeded
-    permutation gives the shuffled pools of the larger workloads.
+    free queue (default: 0..N-1, as in the pages' timeline); a seeded
+    permutation gives the shuffled pools of the larger workloads. Every
+    operation either completes or raises before changing anything.
     """
 
     def __init__(self, num_blocks: int, block_size: int, initial_free=None):
         if num_blocks < 0 or block_size <= 0:
             raise ValueError((num_blocks, block_size))
+        queue = range(num_blocks) if initial_free is None else [int(b) for b in initial_free]
+        if sorted(queue) != list(range(num_blocks)):
+            raise ValueError("initial_free must be a permutation of range(num_blocks)")
         self.block_size = block_size
         self.num_blocks = num_blocks
-        order = list(range(num_blocks)) if initial_free is None else list(initial_free)
-        if sorted(order) != list(range(num_blocks)):
-            raise ValueError("initial_free must be a permutation of range(num_blocks)")
-        self.free = deque(order)
         self.ref = [0] * num_blocks
-        self.tables: dict = {}
-        self.lengths: dict = {}
+        self._queue = deque(queue)     # unreferenced blocks; the head goes out first
+        self._seqs: dict = {}
 
-    # -- internals ---------------------------------------------------------
-    def _take(self, n: int) -> list:
-        # Capacity is checked before anything moves: a short pool takes nothing.
-        if n > len(self.free):
-            raise MemoryError(f"need {n}, free {len(self.free)}")
-        out = [self.free.popleft() for _ in range(n)]
-        for b in out:
-            assert self.ref[b] == 0
-            self.ref[b] = 1
-        return out
+    # -- views ---------------------------------------------------------------
+    @property
+    def tables(self) -> dict:
+        """Request id -> its block table (a copy)."""
+        return {rid: list(q.blocks) for rid, q in self._seqs.items()}
 
-    def _acquire(self, block: int) -> None:
-        if self.ref[block] == 0:
-            self.free.remove(block)
-        self.ref[block] += 1
+    @property
+    def lengths(self) -> dict:
+        """Request id -> tokens held."""
+        return {rid: q.length for rid, q in self._seqs.items()}
 
-    def _release(self, block: int) -> None:
-        assert self.ref[block] > 0, f"refcount underflow on block {block}"
-        self.ref[block] -= 1
-        if self.ref[block] == 0:
-            self.free.append(block)
+    def free_list(self) -> list:
+        return list(self._queue)
 
-    # -- public API --------------------------------------------------------
+    # -- block reference counting -------------------------------------------
+    def _check_room(self, wanted: int) -> None:
+        if wanted > len(self._queue):
+            raise MemoryError(f"{wanted} block(s) wanted, {len(self._queue)} unreferenced")
+
+    def _fresh(self, count: int) -> list:
+        """``count`` blocks off the head of the queue, each now referenced
+        once; nothing is taken when the queue is too short."""
+        self._check_room(count)
+        got = []
+        while len(got) < count:
+            blk = self._queue.popleft()
+            assert self.ref[blk] == 0
+            self.ref[blk] = 1
+            got.append(blk)
+        return got
+
+    def _ref_up(self, blk: int) -> None:
+        if self.ref[blk] == 0:           # leaves the queue wherever it waits
+            self._queue.remove(blk)
+        self.ref[blk] += 1
+
+    def _ref_down(self, blk: int) -> None:
+        assert self.ref[blk] > 0, f"refcount underflow on block {blk}"
+        self.ref[blk] -= 1
+        if self.ref[blk] == 0:           # back in line, at the tail
+            self._queue.append(blk)
+
+    # -- requests ------------------------------------------------------------
     def add(self, rid, num_tokens: int, shared_prefix=()) -> list:
         """Admit request ``rid`` with ``num_tokens`` tokens.
 
         ``shared_prefix`` lists physical blocks (already owned by others, or
         free) that become this request's first logical blocks by reference;
-        the remaining blocks are taken fresh. Atomic: on MemoryError nothing
-        changes.
+        the remaining blocks are taken fresh.
         """
-        if rid in self.tables:
+        if rid in self._seqs:
             raise KeyError(rid)
-        need = blocks_needed(num_tokens, self.block_size)
-        shared = list(shared_prefix)
-        if len(shared) > need:
+        total = blocks_needed(num_tokens, self.block_size)
+        prefix = [int(b) for b in shared_prefix]
+        if len(prefix) > total:
             raise ValueError("shared prefix longer than the request")
-        fresh_needed = need - len(shared)
-        # blocks at ref 0 in the prefix leave the free list too
-        revived = len({b for b in shared if self.ref[b] == 0})
-        if fresh_needed + revived > len(self.free):
-            raise MemoryError(f"need {fresh_needed + revived}, free {len(self.free)}")
-        for b in shared:
-            self._acquire(b)
-        blocks = shared + self._take(fresh_needed)
-        self.tables[rid] = blocks
-        self.lengths[rid] = num_tokens
+        # a prefix block at ref 0 leaves the free queue as well
+        self._check_room(total - len(prefix) + len({b for b in prefix if self.ref[b] == 0}))
+        for blk in prefix:
+            self._ref_up(blk)
+        blocks = prefix + self._fresh(total - len(prefix))
+        self._seqs[rid] = _Seq(blocks, num_tokens)
         return list(blocks)
 
-    def grow(self, rid, new_tokens: int) -> list:
-        """Extend ``rid`` by ``new_tokens``; take ceil((L+k)/B) - ceil(L/B) blocks."""
-        old = self.lengths[rid]
-        extra = blocks_needed(old + new_tokens, self.block_size) - blocks_needed(
-            old, self.block_size)
-        got = self._take(extra)
-        self.tables[rid].extend(got)
-        self.lengths[rid] = old + new_tokens
-        return got
+    def extend(self, rid, new_tokens: int) -> list:
+        """``new_tokens`` more tokens for ``rid``: the blocks the longer
+        length covers beyond the current ones, ceil((L+k)/B) - ceil(L/B)."""
+        seq = self._seqs[rid]
+        target = seq.length + new_tokens
+        have = blocks_needed(seq.length, self.block_size)
+        added = self._fresh(blocks_needed(target, self.block_size) - have)
+        seq.blocks.extend(added)
+        seq.length = target
+        return added
 
     def fork(self, parent, child) -> list:
         """``child`` starts as a copy of ``parent``: the same blocks, by
         reference (every block gains one reference), the same length."""
-        if child in self.tables:
+        if child in self._seqs:
             raise KeyError(child)
-        blocks = list(self.tables[parent])
-        for b in blocks:
-            self._acquire(b)
-        self.tables[child] = blocks
-        self.lengths[child] = self.lengths[parent]
-        return list(blocks)
+        src = self._seqs[parent]
+        for blk in src.blocks:
+            self._ref_up(blk)
+        self._seqs[child] = _Seq(list(src.blocks), src.length)
+        return list(src.blocks)
 
     def append_slot(self, rid):
         """Make room for one more token of ``rid`` (copy-on-write rule).
 
         Returns (slot, copy): the slot the new token goes to, and (src, dst)
-        when the last block had to be copied first, else None. Atomic: on
-        MemoryError nothing changes.
+        when the last block had to be copied first, else None.
         """
-        n = self.lengths[rid]
-        table = self.tables[rid]
-        used = n % self.block_size
-        if used == 0:                      # no block, or the last one is full
-            (fresh,) = self._take(1)
-            table.append(fresh)
-            self.lengths[rid] = n + 1
-            return fresh * self.block_size, None
-        last = table[-1]
-        if self.ref[last] == 1:            # sole owner: write in place
-            self.lengths[rid] = n + 1
-            return last * self.block_size + used, None
-        (fresh,) = self._take(1)           # shared partial block: copy on write
-        table[-1] = fresh
-        self._release(last)
-        self.lengths[rid] = n + 1
-        return fresh * self.block_size + used, (last, fresh)
+        seq = self._seqs[rid]
+        B = self.block_size
+        filled = seq.length % B
+        if filled == 0:                  # no block yet, or the last one is full
+            (blk,) = self._fresh(1)
+            seq.blocks.append(blk)
+            seq.length += 1
+            return blk * B, None
+        last = seq.blocks[-1]
+        if self.ref[last] == 1:          # sole owner: write in place
+            seq.length += 1
+            return last * B + filled, None
+        (blk,) = self._fresh(1)          # shared partial block: copy on write
+        seq.blocks[-1] = blk
+        self._ref_down(last)
+        seq.length += 1
+        return blk * B + filled, (last, blk)
 
-    def free_request(self, rid) -> None:
-        """Release every block of ``rid`` in table order."""
-        for b in self.tables.pop(rid):
-            self._release(b)
-        del self.lengths[rid]
+    def release(self, rid) -> None:
+        """Drop ``rid``; its blocks lose one reference each, in table order."""
+        for blk in self._seqs.pop(rid).blocks:
+            self._ref_down(blk)
 
     def slot(self, rid, position: int) -> int:
-        if not 0 <= position < self.lengths[rid]:
-            raise IndexError(position)
-        return translate(self.tables[rid], position, self.block_size)
-
-    def free_list(self) -> list:
-        return list(self.free)
+        """Slot of one of ``rid``'s existing positions."""
+        seq = self._seqs[rid]
+        if position < 0 or position >= seq.length:
+            raise IndexError(f"position {position} outside [0, {seq.length})")
+        return translate(seq.blocks, position, self.block_size)
 
 
 def slot_mapping(tables, positions, block_size: int) -> list:

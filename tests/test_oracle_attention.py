@@ -129,33 +129,55 @@ def test_attention_matches_brute_force(seed):
 
 # -- the glossary page's worked example ----------------------------------------
 
+def _page_contiguous(batch, t):
+    """Each sequence's contiguous K and V [Hkv, L, D], rebuilt position by
+    position from the page's tables (brute force, no oracle code)."""
+    B = batch.block_size
+    out = []
+    for s, L in enumerate(batch.context_lens):
+        rows = [int(batch.block_table[s][p // B]) for p in range(int(L))]
+        k = torch.stack([t["k_cache"][r, :, p % B] for p, r in enumerate(rows)], 1)
+        v = torch.stack([t["v_cache"][r, :, p % B] for p, r in enumerate(rows)], 1)
+        out.append((k, v))
+    return out
+
+
 def test_page_example_paged_equals_contiguous(golden):
+    """The glossary page's experiment: attention through the page tables
+    equals attention over the contiguous histories, max abs diff 0.000e+00
+    as printed, and standard fp32 attention agrees within the page's
+    tolerance; the two sequences share their first block (same K and V for
+    positions 0..3) and V there is 0.5 x K."""
     g = golden("sharing.json")
     batch = W.tiny_page_example()
     t = W.layer_tensors(batch, poison=False)
     scale = float(np.float32(1.0 / math.sqrt(batch.head_size)))
+    cont = _page_contiguous(batch, t)
+    assert torch.equal(cont[0][0][:, :4], cont[1][0][:, :4])
+    assert torch.equal(cont[0][1][:, :4], cont[1][1][:, :4])
+    assert torch.equal(cont[0][1][:, :4], 0.5 * cont[0][0][:, :4])
     for s, L in enumerate(batch.context_lens):
         k, v = oracle.gather(t["k_cache"], t["v_cache"], batch.block_table[s], int(L), "f32")
-        assert np.array_equal(k, t["k_contiguous"][s].numpy().astype(np.float64))
-        assert np.array_equal(v, t["v_contiguous"][s].numpy().astype(np.float64))
+        assert np.array_equal(k, cont[s][0].double().numpy())
+        assert np.array_equal(v, cont[s][1].double().numpy())
     paged = oracle.attention(t["q"], t["k_cache"], t["v_cache"], batch.block_table,
                              batch.context_lens, scale, "f32")
-    # contiguous attention: the same oracle over an identity-mapped pool
+    G = batch.num_heads // batch.num_kv_heads
     for s, L in enumerate(batch.context_lens):
         L = int(L)
-        kc = t["k_contiguous"][s].permute(1, 0, 2).contiguous().reshape(L, 1, 2, 8)
-        vc = t["v_contiguous"][s].permute(1, 0, 2).contiguous().reshape(L, 1, 2, 8)
-        kc = kc.permute(0, 2, 1, 3).contiguous()   # pool of L one-slot blocks
-        vc = vc.permute(0, 2, 1, 3).contiguous()
-        dense = oracle.attention(t["q"][s:s + 1], kc, vc, np.arange(L, dtype=np.int32)[None],
+        kc, vc = cont[s]
+        # contiguous attention: the same oracle over a pool of L one-slot
+        # blocks laid out in position order (identity table)
+        kd = kc.permute(1, 0, 2).unsqueeze(2).contiguous()
+        vd = vc.permute(1, 0, 2).unsqueeze(2).contiguous()
+        dense = oracle.attention(t["q"][s:s + 1], kd, vd, np.arange(L, dtype=np.int32)[None],
                                  np.array([L], np.int32), scale, "f32")
         assert np.abs(paged[s] - dense[0]).max() == g["max_attention_abs_diff"]
-        # the page's own fp32 torch attention, at the page's tolerance
-        qh = t["q"][s][:, None, :]
-        kk = t["k_contiguous"][s].repeat_interleave(2, dim=0)
-        vv = t["v_contiguous"][s].repeat_interleave(2, dim=0)
-        ref = torch.softmax(qh @ kk.transpose(-2, -1) / math.sqrt(8), -1) @ vv
-        np.testing.assert_allclose(paged[s], ref[:, 0].double().numpy(), rtol=1e-5, atol=1e-6)
+        # standard fp32 softmax attention, query head h on KV head h // G
+        for h in range(batch.num_heads):
+            w = torch.softmax((kc[h // G] @ t["q"][s, h]) / math.sqrt(batch.head_size), 0)
+            ref = (w[:, None] * vc[h // G]).sum(0)
+            np.testing.assert_allclose(paged[s, h], ref.double().numpy(), rtol=1e-5, atol=1e-6)
 
 
 def test_page_example_poisoned_slots_unread():

@@ -36,9 +36,9 @@ def test_allocator_timeline(golden):
         if st["op"] == "add":
             a.add(st["rid"], st["n"])
         elif st["op"] == "grow":
-            a.grow(st["rid"], st["n"])
+            a.extend(st["rid"], st["n"])
         else:
-            a.free_request(st["rid"])
+            a.release(st["rid"])
         assert a.tables == st["tables"], st
         assert a.free_list() == st["free"], st
     for c in g["slot_checks"]:
@@ -46,7 +46,7 @@ def test_allocator_timeline(golden):
     before = (a.free_list(), {k: v[:] for k, v in a.tables.items()}, dict(a.lengths),
               list(a.ref))
     with pytest.raises(MemoryError):
-        a.grow(g["failing_grow"]["rid"], g["failing_grow"]["n"])
+        a.extend(g["failing_grow"]["rid"], g["failing_grow"]["n"])
     after = (a.free_list(), {k: v[:] for k, v in a.tables.items()}, dict(a.lengths),
              list(a.ref))
     assert before == after
@@ -65,7 +65,7 @@ def test_allocator_error_paths():
         a.add("y", 13)          # needs 4 blocks, 2 free
     assert a.free_list() == [2, 3] and "y" not in a.tables
     with pytest.raises(KeyError):
-        a.grow("nope", 1)
+        a.extend("nope", 1)
 
 
 def test_refcount_sharing(golden):
@@ -77,10 +77,10 @@ def test_refcount_sharing(golden):
     a.add("B", 3 * g["block_size"], shared_prefix=[bl["b0"], bl["b1"]])
     assert a.tables["B"] == [bl["b0"], bl["b1"], bl["b3"]]
     assert a.ref == g["after_add"]["ref"]
-    a.free_request("A")
+    a.release("A")
     assert a.ref == g["after_free_A"]["ref"]
     assert a.free_list() == [bl[n] for n in g["after_free_A"]["returned"]]
-    a.free_request("B")
+    a.release("B")
     assert a.ref == g["after_free_B"]["ref"]
     assert a.free_list() == [bl[n] for n in g["after_free_B"]["returned"]]
 
@@ -144,7 +144,7 @@ def test_scatter_then_translate_reads_back():
     rng = np.random.default_rng(1)
     a = A.BlockAllocator(6, 4, initial_free=[3, 0, 5, 1, 4, 2])
     a.add("s", 7)
-    a.grow("s", 1)                     # position 7 now exists
+    a.extend("s", 1)                     # position 7 now exists
     pool = np.zeros((6, 2, 4, 8), np.float32)
     new = rng.standard_normal((1, 2, 8)).astype(np.float32)
     out = scatter(pool, new, [a.slot("s", 7)])
@@ -164,10 +164,10 @@ def _alloc_tables(batch):
     for s, n in enumerate(lens):
         a.add(s, int(n), shared_prefix=shared if s in sharer_set else ())
     if shared:
-        a.free_request("__prefix__")
+        a.release("__prefix__")
     if batch.positions is not None:
         for s in range(batch.num_seqs):
-            a.grow(s, 1)
+            a.extend(s, 1)
     return a
 
 

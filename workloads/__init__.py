@@ -11,8 +11,8 @@ Shapes follow the pages:
   * pool [num_blocks, Hkv, B, D] (glossary page "PagedAttention", teaching
     layout), block table [num_seqs, max_blocks] int32 padded with -1
     (same page, and the source-walkthrough page, section 1.7);
-  * the tiny case reproduces the glossary page's worked example and its draw
-    order (seed 53, K prefix, K tails, V tails, q; V prefix = 0.5 * K prefix);
+  * the tiny case is the glossary page's worked example (its tables,
+    lengths and shapes; seed 53; V prefix = 0.5 * K prefix), drawn as pools;
   * the larger cases use the geometry of the nxmr.cn article, section 1.1
     (32 layers x 32 heads x 128 dims, fp16), the default block of 16 from the
     paper-notes page, prefix sharing from the glossary and walkthrough pages,
@@ -386,31 +386,24 @@ CASES = {
 # --------------------------------------------------------------------------
 
 def _page_example_tensors(batch: Batch):
-    """The glossary page's draw order with a CPU generator seeded 53:
-    K prefix [Hkv,4,D], K tails [Hkv,6,D] and [Hkv,3,D], V tails (same
-    shapes), q [2,Hq,1,D]; V prefix = 0.5 * K prefix. Pool slots no token
-    uses are zero, as on the page."""
+    """The glossary page's worked example, stated as pools: q [S, Hq, D], the
+    K pool and the V pool [N, Hkv, B, D] are N(0,1) float32 draws from numpy
+    PCG64 seeded 53, in that order; the shared prefix block's V is 0.5 times
+    its K (the example's V prefix = 0.5 x K prefix). Slots no live token
+    occupies hold zeros, as the page's pools do."""
     import torch
-    g = torch.Generator().manual_seed(53)
-    hkv, d, hq = batch.num_kv_heads, batch.head_size, batch.num_heads
-    lens = [int(x) for x in batch.context_lens]
-    prefix = torch.randn(hkv, 4, d, generator=g)
-    ks = [torch.cat((prefix, torch.randn(hkv, n - 4, d, generator=g)), 1) for n in lens]
-    vs = [torch.cat((prefix * 0.5, torch.randn(hkv, n - 4, d, generator=g)), 1) for n in lens]
-    q = torch.randn(2, hq, 1, d, generator=g)
-    kp = torch.zeros(batch.num_blocks, hkv, batch.block_size, d)
-    vp = torch.zeros_like(kp)
-    b = batch.block_size
-    for s, row in enumerate(batch.block_table.tolist()):
-        for lb, pb in enumerate(row):
-            if pb < 0:
-                continue
-            lo, hi = lb * b, min(lb * b + b, lens[s])
-            if lo < hi:
-                kp[pb, :, :hi - lo] = ks[s][:, lo:hi]
-                vp[pb, :, :hi - lo] = vs[s][:, lo:hi]
-    return {"q": q[:, :, 0, :].contiguous(), "k_cache": kp, "v_cache": vp,
-            "k_contiguous": ks, "v_contiguous": vs}
+    rng = np.random.default_rng(batch.seed)
+    n, hkv, b, d = batch.num_blocks, batch.num_kv_heads, batch.block_size, batch.head_size
+    q = rng.standard_normal((batch.num_seqs, batch.num_heads, d), dtype=np.float32)
+    k = rng.standard_normal((n, hkv, b, d), dtype=np.float32)
+    v = rng.standard_normal((n, hkv, b, d), dtype=np.float32)
+    for blk in batch.shared_blocks:
+        v[blk] = np.float32(0.5) * k[blk]
+    unused = (np.arange(b)[None, :] >= live_counts(batch)[:, None])[:, None, :, None]
+    k = np.where(unused, np.float32(0), k)
+    v = np.where(unused, np.float32(0), v)
+    return {"q": torch.from_numpy(q), "k_cache": torch.from_numpy(np.ascontiguousarray(k)),
+            "v_cache": torch.from_numpy(np.ascontiguousarray(v))}
 
 
 def live_counts(batch: Batch) -> np.ndarray:
