@@ -74,38 +74,71 @@ def traffic_for(workload: str, kernel: str = "decode_split", sources=DECODE_SOUR
     return rec.get("hbm_bytes_per_launch")
 
 
-def read_ceiling(dev, nbytes: float = 0.0, reps: int = 5):
-    """Measured streaming-read ceiling of this device for the split decode
-    kernel's stream shape (the library's read probe: 8 KiB tiles, 4 KiB from
-    each of two buffers of at least 2 GiB, distinct tiles in a seeded shuffled
-    order, non-temporal 16-byte loads, each wave reading a contiguous run),
-    over nbytes (the kernel's own bytes per launch; 4 GiB if 0): median GB/s.
-    A short stream pays the same start and drain as a short kernel."""
+PROBE_LIB = os.path.join(ROOT, "paged_kv_cache_113_amd", "libpkvprobe.so")
+_probe = None
+
+
+def probe_lib():
+    """The bench-only read-stream probe library (built beside libpagedkv.so)."""
+    global _probe
+    if _probe is None:
+        import ctypes
+        if not os.path.exists(PROBE_LIB):
+            raise ImportError(f"{PROBE_LIB} is missing: build with python __graft_entry__.py")
+        lib = ctypes.CDLL(PROBE_LIB)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.pkvprobe_read_stream.restype = I32
+        lib.pkvprobe_read_stream.argtypes = [P, P, I64, P, I64, I32, I32, I32, P, P]
+        _probe = lib
+    return _probe
+
+
+def run_read_probe(k, v, order, heads, tiles_per_head, wg_per_cu, sink):
+    import ctypes
     import torch
-    import paged_kv_cache_113_amd as pkv
-    n = int(nbytes // 8192) if nbytes > 0 else 1 << 19
-    tiles = max(n, 1 << 19)
-    a = torch.empty(tiles * 4096, dtype=torch.uint8, device=dev)
-    b = torch.empty_like(a)
-    a.fill_(1)
-    b.fill_(2)
+    nbytes = k.numel() * k.element_size()
+    assert v.numel() * v.element_size() == nbytes and order.dtype == torch.int32
+    rc = probe_lib().pkvprobe_read_stream(
+        ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()), nbytes,
+        ctypes.c_void_p(order.data_ptr()), order.numel(), heads, tiles_per_head, wg_per_cu,
+        ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"pkvprobe_read_stream failed: {rc}")
+
+
+def read_probe(dev, nbytes, heads, tiles_per_head, wg_per_cu, reps: int = 5):
+    """Read rate of the split decode kernel's access pattern without its
+    arithmetic (the bench-only probe library): nbytes of K and V read as
+    whole blocks of `heads` side-by-side KV-head slabs (tiles_per_head 4 KiB
+    tiles each), distinct blocks in a seeded shuffled order over pools of at
+    least 2 GiB each, neighbouring waves reading the slabs of one block, the
+    kernel's launch shape, load width, loads in flight and non-temporal
+    hint. Median GB/s over ``reps`` calls."""
+    import torch
+    block = 4096 * heads * tiles_per_head
+    n = max(1, int(nbytes // (2 * block)))
+    pool_blocks = max(n, (2 << 30) // block)
+    k = torch.empty(pool_blocks * block, dtype=torch.uint8, device=dev)
+    v = torch.empty_like(k)
+    k.fill_(1)
+    v.fill_(2)
     order = torch.from_numpy(
-        np.random.default_rng(7).permutation(tiles)[:n].astype(np.int32)).to(dev)
+        np.random.default_rng(7).permutation(pool_blocks)[:n].astype(np.int32)).to(dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     for _ in range(2):
-        pkv.stream_read_probe(a, b, order, sink)
+        run_read_probe(k, v, order, heads, tiles_per_head, wg_per_cu, sink)
     ts = []
     for _ in range(reps):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        pkv.stream_read_probe(a, b, order, sink)
+        run_read_probe(k, v, order, heads, tiles_per_head, wg_per_cu, sink)
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
-    del a, b, order, sink
+    del k, v, order, sink
     torch.cuda.empty_cache()
-    return 8192.0 * n / (float(np.median(ts)) / 1e3) / 1e9
+    return 2.0 * block * n / (float(np.median(ts)) / 1e3) / 1e9
 
 
 def kv_bytes(batch, lens) -> float:
@@ -369,11 +402,54 @@ def visible_pairs_of(batch, s) -> int:
     return q * (c - q) + q * (q + 1) // 2
 
 
-def cpu_baseline(batch, th, target_s: float, threads: int):
+def host_topology() -> dict:
+    """Logical CPUs (nproc), the CPUs this process may run on, physical cores
+    and sockets (from /proc/cpuinfo, or lscpu when present), and the thread
+    share the job is given (OMP_NUM_THREADS when set)."""
+    import shutil
+    import subprocess
+    info = {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "physical_cores": None, "sockets": None, "model": None,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+    try:
+        cores, sockets, phys = set(), set(), None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "physical id":
+                    phys = val
+                    sockets.add(val)
+                elif key == "core id":
+                    cores.add((phys, val))
+                elif key == "model name" and info["model"] is None:
+                    info["model"] = val
+        if cores:
+            info["physical_cores"] = len(cores)
+        if sockets:
+            info["sockets"] = len(sockets)
+    except OSError:
+        pass
+    if shutil.which("lscpu"):
+        try:
+            out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+            kv = {a.strip(): b.strip() for a, _, b in
+                  (line.partition(":") for line in out.splitlines())}
+            per = kv.get("Core(s) per socket")
+            sk = kv.get("Socket(s)")
+            if per and sk and per.isdigit() and sk.isdigit():
+                info["physical_cores"] = int(per) * int(sk)
+                info["sockets"] = int(sk)
+        except (OSError, subprocess.SubprocessError):
+            pass
+    return info
+
+
+def cpu_baseline(batch, th, target_s: float, threads: int, topo: dict):
     """Time the fp64 oracle on layer 0 of the workload (post-write pools made
-    by the oracle's own scatter): all sequences with ``threads`` workers,
-    repeated to about target_s / 2, and one worker on a prefix of a seeded
-    sequence order sized to about target_s / 2."""
+    by the oracle's own scatter), median of 3 runs per leg: all sequences with
+    ``threads`` workers (the job's thread share), and one worker on a prefix of
+    a seeded sequence order sized to about target_s / 6 per run."""
     import oracle
     k = oracle._raw(th["k_cache"], batch.dtype)
     v = oracle._raw(th["v_cache"], batch.dtype)
@@ -402,11 +478,9 @@ def cpu_baseline(batch, th, target_s: float, threads: int):
         return time.perf_counter() - t0
 
     everything = np.arange(batch.num_seqs, dtype=np.int32)
-    reps, spent = 0, 0.0
-    while spent < target_s / 2 or reps == 0:
-        spent += run(everything, threads)
-        reps += 1
-    all_rate = kv_bytes(batch, batch.context_lens) * reps / spent
+    all_runs = [run(everything, threads) for _ in range(3)]
+    all_s = float(np.median(all_runs))
+    all_rate = kv_bytes(batch, batch.context_lens) / all_s
     order = np.random.default_rng(7).permutation(batch.num_seqs).astype(np.int32)
     # work per sequence: the positions its query rows attend
     work = batch.context_lens.astype(np.int64) if batch.query_lens is None else np.array(
@@ -415,18 +489,22 @@ def cpu_baseline(batch, th, target_s: float, threads: int):
     dt = run(probe, 1)
     per_pos = dt / max(1, int(work[probe].sum()))
     csum = np.cumsum(work[order])
-    n1 = int(max(1, min(len(order), np.searchsorted(csum, (target_s / 2) / per_pos) + 1)))
-    dt1 = run(order[:n1], 1)
+    n1 = int(max(1, min(len(order), np.searchsorted(csum, (target_s / 6) / per_pos) + 1)))
+    one_runs = [run(order[:n1], 1) for _ in range(3)]
+    dt1 = float(np.median(one_runs))
     one_rate = kv_bytes(batch, batch.context_lens[order[:n1]]) / dt1
     pos = float(batch.context_lens.sum())
     return {"value": round(all_rate / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"layer 0 of the workload, all {batch.num_seqs} sequences "
-                      f"({int(pos)} positions) x {reps} repeats in {spent:.1f} s; "
-                      f"fp64 gather + attention",
-            "seq_tokens_per_s": round(pos * reps / spent, 1),
-            "single_thread": {"value": round(one_rate / 1e9, 4), "unit": "GB/s",
-                              "sample": f"{n1} sequences of layer 0, {dt1:.1f} s"}}
+                      f"({int(pos)} positions), median of 3 runs "
+                      f"({', '.join(f'{x:.2f}' for x in all_runs)} s); fp64 gather + attention",
+            "seq_tokens_per_s": round(pos / all_s, 1),
+            "threads": threads,
+            "host": topo,
+            "single_thread": {"value": round(one_rate / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"{n1} sequences of layer 0, median of 3 runs "
+                                        f"({', '.join(f'{x:.2f}' for x in one_runs)} s)"}}
 
 
 def main():
@@ -450,8 +528,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured in a HIP graph (per-kernel times "
                          "still come from eager steps)")
-    ap.add_argument("--no-ceiling", action="store_true",
-                    help="skip the streaming-read ceiling probe")
+    ap.add_argument("--no-probe", "--no-ceiling", dest="no_probe", action="store_true",
+                    help="skip the read-stream probe")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -652,14 +730,26 @@ def main():
     pairs = float(visible_pairs(batch).sum()) if varlen else positions
     flops = 4.0 * batch.num_heads * batch.head_size * pairs   # q.K and P.V, per layer
 
-    ceiling = None if args.no_ceiling else read_ceiling(dev, layer_bytes)
+    probe = None
+    if not args.no_probe:
+        G = batch.num_heads // batch.num_kv_heads
+        tph = max(1, batch.block_size * batch.head_size * 2 // 4096)
+        probe = read_probe(dev, layer_bytes, batch.num_kv_heads, tph,
+                           1 if (varlen or G >= 4) else 2)
 
     cpu = None
     if cpu_host is not None:
-        threads = min(os.cpu_count() or 1, 16)
-        print(f"[bench] cpu baseline: oracle, {threads} threads, ~{args.cpu_seconds:.0f} s",
-              file=sys.stderr, flush=True)
-        cpu = cpu_baseline(batch, cpu_host, args.cpu_seconds, threads)
+        # every CPU this process may run on, within the thread share the job
+        # is given (OMP_NUM_THREADS, when the host sets one)
+        topo = host_topology()
+        threads = topo["affinity"]
+        share = topo["omp_num_threads"]
+        if share and share.isdigit() and int(share) > 0:
+            threads = min(threads, int(share))
+        print(f"[bench] cpu baseline: oracle, {threads} threads (nproc {topo['nproc']}, "
+              f"affinity {topo['affinity']}, physical cores {topo['physical_cores']}, sockets "
+              f"{topo['sockets']}), ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(batch, cpu_host, args.cpu_seconds, threads, topo)
 
     config = {"workload": args.workload, "num_seqs": batch.num_seqs, "layers": L,
               "num_heads": batch.num_heads, "num_kv_heads": batch.num_kv_heads,
@@ -697,13 +787,14 @@ def main():
                      else "decode_split_kernel" if P > 0 else "decode_whole_kernel",
                      "bytes_per_launch": layer_bytes,
                      "logical_bytes_per_launch": logical_bytes,
-                     "measured_ceiling": None if ceiling is None else {
-                         "gbs": round(ceiling, 2), "frac": round(achieved / ceiling, 4),
-                         "probe": "pkv_stream_read_probe over the kernel's bytes per launch: "
-                                  "distinct 8 KiB tiles (4 KiB from each of two buffers of "
-                                  ">= 2 GiB) in a seeded shuffled order, non-temporal 16-byte "
-                                  "loads, one 4-wave workgroup per CU, each wave reading a "
-                                  "contiguous run with two tiles in flight"},
+                     "read_probe": None if probe is None else {
+                         "gbs": round(probe, 2), "frac": round(achieved / probe, 4),
+                         "probe": "bench-only read-stream probe over the kernel's bytes per "
+                                  "launch, in its access pattern: whole blocks of Hkv "
+                                  "side-by-side KV-head slabs, K and V, distinct blocks in a "
+                                  "seeded shuffled order over >= 2 GiB pools, neighbouring "
+                                  "waves on one block's slabs, the kernel's launch shape, "
+                                  "non-temporal 16-byte loads, two tiles in flight"},
                      "mfma_view": {"flops_per_launch": flops,
                                    "achieved_tflops": round(flops / (dec_ms / 1e3) / 1e12, 2),
                                    "peak_tflops": 2500.0,

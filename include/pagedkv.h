@@ -130,12 +130,18 @@ int paged_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* 
  *   max_logits[s][h][p] = m_p  = max of z_t over the piece,
  *   exp_sums[s][h][p]   = l_p  = sum exp(z_t - m_p)   (>= 1),
  *   tmp_out[s][h][p][:] = o_p  = sum exp(z_t - m_p) V[t] / l_p,
- * or marks the slot unused (l_p = 0, m_p = -inf). `out` is untouched; the
- * caller then calls paged_attention_reduce. Workspace layouts: max_logits and
- * exp_sums [num_seqs, num_heads, max_partitions] float32, tmp_out [num_seqs,
- * num_heads, max_partitions, head_size] float32; see
- * paged_attention_workspace_bytes. (The plain kernel cuts exactly at
- * multiples of partition_size.)
+ * or marks the slot unused (l_p = 0, m_p = -inf). On the fast path the
+ * pieces follow the balanced split, not multiples of partition_size: a
+ * piece may start anywhere, a sequence shorter than partition_size may own
+ * several slots, and which slots a sequence uses depends on the whole batch
+ * and the device; partition_size then only tells the caller how to size
+ * max_partitions. The plain kernel cuts exactly at multiples of
+ * partition_size (piece p = positions [p P, (p+1) P)). Either way every slot
+ * of a sequence with ctx_s >= 1 holds a partial or l_p = 0. `out` is
+ * untouched; the caller then calls paged_attention_reduce. Workspace
+ * layouts: max_logits and exp_sums [num_seqs, num_heads, max_partitions]
+ * float32, tmp_out [num_seqs, num_heads, max_partitions, head_size] float32;
+ * see paged_attention_workspace_bytes.
  *
  * ctx_s == 0 gives out = 0. Preconditions: ctx_s <= max_blocks_per_seq * B
  * (longer contexts are cut there), and in split mode ctx_s <= max_partitions *
@@ -145,7 +151,8 @@ int paged_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* 
  * num_heads / num_kv_heads ratio. The fast path (matrix-core scores, DPP
  * lane broadcasts, balanced persistent split) covers f16/bf16, head_size
  * 128, block_size a multiple of 16, groups of up to 16 query heads per KV
- * head and, in split mode, up to 8192 sequences; other shapes run a plain
+ * head and, in split mode, up to 8192 sequences whose tables hold at most
+ * 2^31 - 1 16-position tiles together; other shapes run a plain
  * wave-per-head kernel.
  * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE (num_heads % num_kv_heads != 0, sizes
  * < 1, partition_size not a positive multiple of block_size, max_partitions
@@ -167,12 +174,15 @@ int paged_decode_attention(float* out, const void* query, const void* k_cache,
  * For each (s, h) with ctx_s >= 1, over the slots p < max_partitions with
  * l_p > 0, M = max_p m_p and w_p = l_p * exp(m_p - M):
  *   out[s][h][:] = sum_p w_p o_p / sum_p w_p,
- * and out = 0 when ctx_s <= 0 or no slot is used (nothing is read then).
- * tmp_out rows of unused slots are never read. The pages name only "a reduce
- * kernel that merges the partitions" (source-walkthrough page, section 1.8);
- * this is the exact log-sum-exp merge of the partials paged_decode_attention
- * writes. partition_size is accepted for symmetry and must be >= 1. Layouts
- * as in paged_decode_attention.
+ * and out = 0 when ctx_s <= 0 or no slot is used. Every one of the row's
+ * max_partitions slots is looked at, whatever ctx_s / partition_size is:
+ * slots marked unused (l_p <= 0, as paged_decode_attention leaves them) are
+ * skipped and their tmp_out rows never read, so the merge takes the
+ * balanced pieces of the fast path and the aligned partitions of the plain
+ * kernel alike. The pages name only "a reduce kernel that merges the
+ * partitions" (source-walkthrough page, section 1.8); this is the exact
+ * log-sum-exp merge. partition_size is not used by the merge (accepted for
+ * symmetry; it must be >= 1). Layouts as in paged_decode_attention.
  * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_LAUNCH. num_seqs == 0 is a
  * no-op.
  */
@@ -411,30 +421,6 @@ int pkv_pool_cache_full_blocks(pkv_block_pool* pool, const int32_t* table,
  * Returns the number of free blocks. */
 int pkv_pool_state(const pkv_block_pool* pool, int32_t* ref_out, int32_t* free_out,
                    uint8_t* cached_out);
-
-/*
- * pkv_stream_read_probe -- a measurement aid, not part of the attention path:
- * the read bandwidth that a read-once stream shaped like the split decode
- * kernel's K/V stream reaches on the current device (the measured ceiling
- * that its rates are compared with, beside the datasheet peak).
- *
- * Reads, for each i < num_tiles, the 4096-byte tile tile_order[i] of a and
- * the tile of b at the same index (8 KiB per i: a K and a V tile); the waves
- * of one 4-wave workgroup per CU each read a contiguous run of the order with
- * two tiles in flight, in 16-byte loads with the non-temporal hint, as the
- * split decode kernel does. a and b: device buffers of buffer_bytes each (a
- * multiple of 4096); tile_order: device int32 [num_tiles] (an index outside
- * [0, buffer_bytes / 4096) reads tile 0; a wave given a single tile reads it
- * twice); sink: 16 bytes of device memory,
- * written only on a data-dependent condition that keeps the loads (its
- * contents mean nothing). The caller owns every buffer and times the call on
- * its stream: bytes read = 8192 * num_tiles.
- * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_LAUNCH. num_tiles == 0 is a
- * no-op.
- */
-int pkv_stream_read_probe(const void* a, const void* b, int64_t buffer_bytes,
-                          const int32_t* tile_order, int64_t num_tiles, void* sink,
-                          void* stream);
 
 /* pkv_strerror -- static description of a pkv_status code. */
 const char* pkv_strerror(int code);

@@ -51,7 +51,6 @@ SIGNATURES = {
     "pkv_pool_admit": (_I32, [_P, _P, _I64, _P, _I64, _P, _P]),
     "pkv_pool_cache_full_blocks": (_I32, [_P, _P, _P, _I64, _P, _I64]),
     "pkv_pool_state": (_I32, [_P, _P, _P, _P]),
-    "pkv_stream_read_probe": (_I32, [_P, _P, _I64, _P, _I64, _P, _P]),
     "pkv_strerror": (ctypes.c_char_p, [_I32]),
 }
 
@@ -98,11 +97,44 @@ def _dev(*ts):
             raise ValueError("tensors must be contiguous and on the GPU")
 
 
+def _need(cond, what):
+    """Host-side argument check: the library trusts sizes it is given, so a
+    tensor smaller than they say would be read or written out of bounds."""
+    if not cond:
+        raise ValueError(what)
+
+
+def _pool_geometry(k_cache, v_cache):
+    _need(k_cache.dim() == 4, "pools are [num_blocks, Hkv, B, D]")
+    _need(k_cache.shape == v_cache.shape and k_cache.dtype == v_cache.dtype,
+          "K and V pools differ in shape or dtype")
+    _need(k_cache.dtype in _DTYPE, f"unsupported dtype {k_cache.dtype}")
+    return k_cache.shape
+
+
+def _i32(*ts):
+    for t in ts:
+        _need(t.dtype == torch.int32, "block tables, lengths, positions and query starts are "
+                                      "int32")
+
+
+def _workspace(rows, mp, d, max_logits, exp_sums, tmp_out):
+    for t in (max_logits, exp_sums, tmp_out):
+        _need(t is not None, "the split needs max_logits, exp_sums and tmp_out")
+        _need(t.dtype == torch.float32, "the workspace is float32")
+    _need(max_logits.numel() >= rows * mp and exp_sums.numel() >= rows * mp,
+          f"max_logits / exp_sums need {rows} x {mp} floats")
+    _need(tmp_out.numel() >= rows * mp * d, f"tmp_out needs {rows} x {mp} x {d} floats")
+
+
 def paged_slot_mapping(slot_mapping, block_table, positions, block_size, stream=None):
     """slot_mapping[s] = block_table[s][p // B] * B + p % B, p = positions[s]."""
+    _need(slot_mapping.dtype == torch.int64, "slot_mapping is int64")
+    _i32(block_table, positions)
+    _need(block_table.dim() == 2 and block_table.shape[0] == positions.numel(),
+          "block_table is [num_seqs, max_blocks] with one row per position")
+    _need(slot_mapping.numel() >= positions.numel(), "slot_mapping is shorter than positions")
     _dev(slot_mapping, block_table, positions)
-    assert slot_mapping.dtype == torch.int64 and block_table.dtype == torch.int32
-    assert positions.dtype == torch.int32
     _check("paged_slot_mapping", lib.paged_slot_mapping(
         _ptr(slot_mapping), _ptr(block_table), _ptr(positions), positions.shape[0],
         block_table.shape[1], block_size, _stream(stream)))
@@ -110,10 +142,13 @@ def paged_slot_mapping(slot_mapping, block_table, positions, block_size, stream=
 
 def paged_kv_write(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
     """Store k_new/v_new [T, Hkv, D] at their slots of [N, Hkv, B, D] pools."""
+    n, hkv, b, d = _pool_geometry(k_cache, v_cache)
+    _need(k_new.dim() == 3 and k_new.shape[1:] == (hkv, d) and v_new.shape == k_new.shape,
+          "k_new / v_new are [num_tokens, Hkv, D] of the pools' geometry")
+    _need(k_new.dtype == v_new.dtype == k_cache.dtype, "new K/V and pools differ in dtype")
+    _need(slot_mapping.dtype == torch.int64, "slot_mapping is int64")
+    _need(slot_mapping.numel() >= k_new.shape[0], "slot_mapping is shorter than k_new")
     _dev(k_cache, v_cache, k_new, v_new, slot_mapping)
-    assert k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype
-    assert slot_mapping.dtype == torch.int64
-    n, hkv, b, d = k_cache.shape
     _check("paged_kv_write", lib.paged_kv_write(
         _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
         k_new.shape[0], n, hkv, b, d, _DTYPE[k_cache.dtype], _stream(stream)))
@@ -123,12 +158,23 @@ def paged_decode_attention(out, query, k_cache, v_cache, block_table, context_le
                            partition_size=0, max_partitions=0, max_logits=None,
                            exp_sums=None, tmp_out=None, stream=None):
     """Decode attention; split mode writes the partials (see include/pagedkv.h)."""
+    n, hkv, b, d = _pool_geometry(k_cache, v_cache)
+    _need(query.dim() == 3 and query.shape[2] == d, "query is [num_seqs, Hq, D]")
+    _need(query.dtype == k_cache.dtype, "query and pools differ in dtype")
+    s, hq, _ = query.shape
+    _i32(block_table, context_lens)
+    _need(block_table.dim() == 2 and block_table.shape[0] == s,
+          "block_table is [num_seqs, max_blocks]")
+    _need(context_lens.numel() == s, "context_lens has one entry per sequence")
+    if partition_size > 0:
+        _workspace(s * hq, max_partitions, d, max_logits, exp_sums, tmp_out)
+    else:
+        _need(out is not None, "out is needed without a split")
+    if out is not None:
+        _need(out.dtype == torch.float32 and out.numel() == s * hq * d,
+              "out is float32 [num_seqs, Hq, D]")
     _dev(out, query, k_cache, v_cache, block_table, context_lens, max_logits, exp_sums,
          tmp_out)
-    assert block_table.dtype == torch.int32 and context_lens.dtype == torch.int32
-    assert out is None or out.dtype == torch.float32
-    n, hkv, b, d = k_cache.shape
-    s, hq, _ = query.shape
     _check("paged_decode_attention", lib.paged_decode_attention(
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(context_lens), s, hq, hkv, d, b, n, block_table.shape[1], float(scale),
@@ -139,8 +185,14 @@ def paged_decode_attention(out, query, k_cache, v_cache, block_table, context_le
 def paged_attention_reduce(out, max_logits, exp_sums, tmp_out, context_lens, partition_size,
                            stream=None):
     """Log-sum-exp merge of split partials [S, Hq, P(, D)] into out [S, Hq, D]."""
-    _dev(out, max_logits, exp_sums, tmp_out, context_lens)
+    _need(tmp_out.dim() == 4, "tmp_out is [num_seqs, Hq, max_partitions, D]")
     s, hq, p, d = tmp_out.shape
+    _workspace(s * hq, p, d, max_logits, exp_sums, tmp_out)
+    _need(out.dtype == torch.float32 and out.numel() == s * hq * d,
+          "out is float32 [num_seqs, Hq, D]")
+    _i32(context_lens)
+    _need(context_lens.numel() == s, "context_lens has one entry per sequence")
+    _dev(out, max_logits, exp_sums, tmp_out, context_lens)
     _check("paged_attention_reduce", lib.paged_attention_reduce(
         _ptr(out), _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out), _ptr(context_lens), s, hq,
         d, partition_size, p, _stream(stream)))
@@ -153,12 +205,20 @@ def paged_varlen_attention(out, query, k_cache, v_cache, block_table, query_star
     query_start_loc[s]..query_start_loc[s+1]-1, at the last positions of the
     sequence's context) into out [T, Hq, D]; partials go through the
     workspace [T, Hq, P(, D)]."""
+    n, hkv, b, d = _pool_geometry(k_cache, v_cache)
+    _need(query.dim() == 3 and query.shape[2] == d, "query is [num_tokens, Hq, D]")
+    _need(query.dtype == k_cache.dtype, "query and pools differ in dtype")
+    t, hq, _ = query.shape
+    _i32(block_table, query_start_loc, context_lens)
+    ns = context_lens.numel()
+    _need(block_table.dim() == 2 and block_table.shape[0] == ns,
+          "block_table is [num_seqs, max_blocks]")
+    _need(query_start_loc.numel() == ns + 1, "query_start_loc has num_seqs + 1 entries")
+    _need(out.dtype == torch.float32 and out.numel() == t * hq * d,
+          "out is float32 [num_tokens, Hq, D]")
+    _workspace(t * hq, max_partitions, d, max_logits, exp_sums, tmp_out)
     _dev(out, query, k_cache, v_cache, block_table, query_start_loc, context_lens, max_logits,
          exp_sums, tmp_out)
-    assert block_table.dtype == query_start_loc.dtype == context_lens.dtype == torch.int32
-    assert out.dtype == torch.float32
-    n, hkv, b, d = k_cache.shape
-    t, hq, _ = query.shape
     _check("paged_varlen_attention", lib.paged_varlen_attention(
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(query_start_loc), _ptr(context_lens), context_lens.shape[0], t, hq, hkv, d, b, n,
@@ -202,7 +262,8 @@ def paged_kv_copy_blocks(k_caches, v_caches, block_mapping, stream=None):
     a PoolSet (then v_caches is ignored)."""
     kp, vp, nl, (n, hkv, b, d), dtype = _pools(k_caches, v_caches)
     _dev(block_mapping)
-    assert block_mapping.dtype == torch.int64 and block_mapping.shape[-1] == 2
+    _need(block_mapping.dtype == torch.int64 and block_mapping.dim() == 2 and
+          block_mapping.shape[1] == 2, "block_mapping is int64 [num_pairs, 2]")
     _check("paged_kv_copy_blocks", lib.paged_kv_copy_blocks(
         kp, vp, nl, _ptr(block_mapping), block_mapping.shape[0], n, hkv, b, d,
         _DTYPE[dtype], _stream(stream)))
@@ -219,7 +280,7 @@ def paged_kv_swap_out(host_dst, k_caches, v_caches, block_ids, stream=None):
     layer's K (index 0) and V (index 1) pool. k_caches may be a PoolSet."""
     kp, vp, nl, (n, hkv, b, d), dtype = _pools(k_caches, v_caches)
     _dev(block_ids)
-    assert block_ids.dtype == torch.int64
+    _need(block_ids.dtype == torch.int64, "block_ids is int64")
     hp, nbytes = _host_buf(host_dst, dtype)
     _check("paged_kv_swap_out", lib.paged_kv_swap_out(
         hp, nbytes, kp, vp, nl, _ptr(block_ids), block_ids.numel(), n, hkv, b, d,
@@ -231,7 +292,7 @@ def paged_kv_swap_in(host_src, k_caches, v_caches, block_ids, stream=None):
     k_caches may be a PoolSet."""
     kp, vp, nl, (n, hkv, b, d), dtype = _pools(k_caches, v_caches)
     _dev(block_ids)
-    assert block_ids.dtype == torch.int64
+    _need(block_ids.dtype == torch.int64, "block_ids is int64")
     hp, nbytes = _host_buf(host_src, dtype)
     _check("paged_kv_swap_in", lib.paged_kv_swap_in(
         hp, nbytes, kp, vp, nl, _ptr(block_ids), block_ids.numel(), n, hkv, b, d,
@@ -245,9 +306,16 @@ def paged_attention_workspace_bytes(num_seqs, num_heads, head_size, max_partitio
 
 def paged_kv_gather(k_out, v_out, k_cache, v_cache, block_table, context_lens, stream=None):
     """Contiguous copy [S, Hkv, max_ctx, D] of each sequence's K and V."""
-    _dev(k_out, v_out, k_cache, v_cache, block_table, context_lens)
-    n, hkv, b, d = k_cache.shape
+    n, hkv, b, d = _pool_geometry(k_cache, v_cache)
+    _need(k_out.dim() == 4 and k_out.shape == v_out.shape and k_out.shape[1] == hkv and
+          k_out.shape[3] == d, "k_out / v_out are [num_seqs, Hkv, max_ctx, D]")
+    _need(k_out.dtype == v_out.dtype == k_cache.dtype, "outputs and pools differ in dtype")
     s, _, max_ctx, _ = k_out.shape
+    _i32(block_table, context_lens)
+    _need(block_table.dim() == 2 and block_table.shape[0] == s,
+          "block_table is [num_seqs, max_blocks]")
+    _need(context_lens.numel() == s, "context_lens has one entry per sequence")
+    _dev(k_out, v_out, k_cache, v_cache, block_table, context_lens)
     _check("paged_kv_gather", lib.paged_kv_gather(
         _ptr(k_out), _ptr(v_out), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(context_lens), s, hkv, d, b, n, block_table.shape[1], max_ctx,
@@ -354,19 +422,6 @@ class BlockPool:
         n = lib.pkv_pool_state(self._h, ref, free, cached)
         _check("pkv_pool_state", n if n < 0 else 0)
         return list(ref), list(free[:n]), [bool(c) for c in cached]
-
-
-def stream_read_probe(a, b, tile_order, sink, stream=None):
-    """Read tile tile_order[i] (4 KiB) of a and of b for every i, in the split
-    decode kernel's stream shape: a measurement aid (bytes read = 8192 *
-    len(tile_order)); the caller times the call."""
-    _dev(a, b, tile_order, sink)
-    assert tile_order.dtype == torch.int32 and sink.numel() * sink.element_size() >= 16
-    nbytes = a.numel() * a.element_size()
-    assert b.numel() * b.element_size() == nbytes
-    _check("pkv_stream_read_probe", lib.pkv_stream_read_probe(
-        _ptr(a), _ptr(b), nbytes, _ptr(tile_order), tile_order.numel(), _ptr(sink),
-        _stream(stream)))
 
 
 def pkv_strerror(code):

@@ -1,7 +1,9 @@
 """Build libpagedkv.so (gfx950) in-tree with hipcc.
 
 Every HIP source is compiled to an object in parallel, then linked into
-paged_kv_cache_113_amd/libpagedkv.so. Always recompiles.
+paged_kv_cache_113_amd/libpagedkv.so. The bench's read-stream probe is a
+library of its own (paged_kv_cache_113_amd/libpkvprobe.so, from probe/),
+outside the attention library's ABI. Always recompiles.
 """
 from __future__ import annotations
 
@@ -16,7 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 SOURCES = ["api.cpp", "cache_ops.hip", "decode_fast.hip", "decode_generic.hip", "block_ops.hip",
-           "prefill.hip", "prefix_cache.cpp", "stream_probe.hip"]
+           "prefill.hip", "prefix_cache.cpp"]
+PROBE_SOURCE = os.path.join(HERE, "probe", "stream_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libpkvprobe.so")
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -47,16 +51,21 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [PROBE_SOURCE]))
+    _link(objs[:-1], LIB_PATH, verbose)
+    _link(objs[-1:], PROBE_LIB, verbose)
     return LIB_PATH
 
 

@@ -73,6 +73,65 @@ int swap_common(void* host, int64_t host_bytes, void* const* k_caches, void* con
   return launch_status(pkv::launch_swap(m, out, as_stream(stream)));
 }
 
+// paged_varlen_attention's argument checks (all before any HIP call); fills
+// `a` except the workspace. Returns kLaunch when there is work to launch,
+// else the status to return (PKV_OK for an empty call).
+constexpr int kLaunch = 1;
+
+int varlen_args(pkv::DecodeArgs& a, float* out, const void* query, const void* k_cache,
+                const void* v_cache, const int32_t* block_table,
+                const int32_t* query_start_loc, const int32_t* context_lens, int num_seqs,
+                int num_tokens, int num_heads, int num_kv_heads, int head_size, int block_size,
+                int64_t num_blocks, int max_blocks_per_seq, float scale, int max_partitions,
+                int dtype) {
+  if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_tokens < 0 || num_heads < 1 || num_kv_heads < 1 || head_size < 1 ||
+      block_size < 1 || num_blocks < 1 || max_blocks_per_seq < 1 || max_partitions < 1)
+    return PKV_ERR_SHAPE;
+  if (num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > 0x7fffffff) return PKV_ERR_SHAPE;
+  if (head_size > 256) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_table || !query_start_loc ||
+      !context_lens)
+    return PKV_ERR_NULL;
+  // one 64-lane wave per (row, head) on the plain path and in the merge
+  const int64_t rows = static_cast<int64_t>(num_tokens) * num_heads;
+  if (rows * 64 > 0xffffffffLL) return PKV_ERR_UNSUPPORTED;
+  a.out = out;
+  a.query = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = head_size;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.scale = scale;
+  a.partition_size = 0;
+  a.max_partitions = max_partitions;
+  a.dtype = dtype;
+  a.query_start_loc = query_start_loc;
+  a.num_tokens = num_tokens;
+  return kLaunch;
+}
+
+int varlen_launch(const pkv::DecodeArgs& a, hipStream_t stream) {
+  if (!pkv::fast_varlen_supported(a)) return launch_status(pkv::launch_varlen_generic(a, stream));
+  // sequences with short query sets, then those with long chunks (each
+  // kernel takes its own kind), then the merge of all query rows
+  hipError_t e = pkv::launch_varlen_fast(a, stream);
+  if (e == hipSuccess) e = pkv::launch_prefill_fast(a, stream);
+  if (e != hipSuccess) return PKV_ERR_LAUNCH;
+  return launch_status(pkv::launch_reduce(a.out, a.max_logits, a.exp_sums, a.tmp_out, nullptr,
+                                          a.num_tokens, a.num_heads, a.head_size, 1,
+                                          a.max_partitions, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,55 +236,17 @@ int paged_varlen_attention(float* out, const void* query, const void* k_cache,
                            int max_blocks_per_seq, float scale, int max_partitions,
                            float* max_logits, float* exp_sums, float* tmp_out, int dtype,
                            void* stream) {
-  if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
-  if (num_seqs < 0 || num_tokens < 0 || num_heads < 1 || num_kv_heads < 1 || head_size < 1 ||
-      block_size < 1 || num_blocks < 1 || max_blocks_per_seq < 1 || max_partitions < 1)
-    return PKV_ERR_SHAPE;
-  if (num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
-  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > 0x7fffffff) return PKV_ERR_SHAPE;
-  if (head_size > 256) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
-  if (!out || !query || !k_cache || !v_cache || !block_table || !query_start_loc ||
-      !context_lens)
-    return PKV_ERR_NULL;
-  if (!max_logits || !exp_sums || !tmp_out) return PKV_ERR_WORKSPACE;
-  // one 64-lane wave per (row, head) on the plain path and in the merge
-  const int64_t rows = static_cast<int64_t>(num_tokens) * num_heads;
-  if (rows * 64 > 0xffffffffLL) return PKV_ERR_UNSUPPORTED;
-
   pkv::DecodeArgs a{};
-  a.out = out;
-  a.query = query;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_table = block_table;
-  a.context_lens = context_lens;
-  a.num_seqs = num_seqs;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_size = head_size;
-  a.block_size = block_size;
-  a.num_blocks = num_blocks;
-  a.max_blocks = max_blocks_per_seq;
-  a.scale = scale;
-  a.partition_size = 0;
-  a.max_partitions = max_partitions;
+  const int rc = varlen_args(a, out, query, k_cache, v_cache, block_table, query_start_loc,
+                             context_lens, num_seqs, num_tokens, num_heads, num_kv_heads,
+                             head_size, block_size, num_blocks, max_blocks_per_seq, scale,
+                             max_partitions, dtype);
+  if (rc != kLaunch) return rc;
+  if (!max_logits || !exp_sums || !tmp_out) return PKV_ERR_WORKSPACE;
   a.max_logits = max_logits;
   a.exp_sums = exp_sums;
   a.tmp_out = tmp_out;
-  a.dtype = dtype;
-  a.query_start_loc = query_start_loc;
-  a.num_tokens = num_tokens;
-  if (!pkv::fast_varlen_supported(a))
-    return launch_status(pkv::launch_varlen_generic(a, as_stream(stream)));
-  // sequences with short query sets, then those with long chunks (each
-  // kernel takes its own kind), then the merge of all query rows
-  hipError_t e = pkv::launch_varlen_fast(a, as_stream(stream));
-  if (e == hipSuccess) e = pkv::launch_prefill_fast(a, as_stream(stream));
-  if (e != hipSuccess) return PKV_ERR_LAUNCH;
-  return launch_status(pkv::launch_reduce(out, max_logits, exp_sums, tmp_out, nullptr,
-                                          num_tokens, num_heads, head_size, 1, max_partitions,
-                                          as_stream(stream)));
+  return varlen_launch(a, as_stream(stream));
 }
 
 int paged_kv_copy_blocks(void* const* k_caches, void* const* v_caches, int num_layers,
@@ -285,16 +306,6 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v
                                              context_lens, num_seqs, num_kv_heads, head_size,
                                              block_size, num_blocks, max_blocks_per_seq, max_ctx,
                                              eb, as_stream(stream)));
-}
-
-int pkv_stream_read_probe(const void* a, const void* b, int64_t buffer_bytes,
-                          const int32_t* tile_order, int64_t num_tiles, void* sink,
-                          void* stream) {
-  if (buffer_bytes < 4096 || buffer_bytes % 4096 != 0 || num_tiles < 0) return PKV_ERR_SHAPE;
-  if (num_tiles == 0) return PKV_OK;
-  if (!a || !b || !tile_order || !sink) return PKV_ERR_NULL;
-  return launch_status(pkv::launch_stream_probe(a, b, buffer_bytes, tile_order, num_tiles, sink,
-                                                as_stream(stream)));
 }
 
 const char* pkv_strerror(int code) {

@@ -766,8 +766,13 @@ bool fast_decode_supported(const DecodeArgs& a) {
   if (!((a.dtype == 1 || a.dtype == 2) && a.head_size == kD && a.block_size % kTile == 0 &&
         G >= 1 && G <= 16 && items <= 0x7fffffff))
     return false;
-  // the split kernel keeps a per-sequence prefix in LDS
-  return a.partition_size == 0 || a.num_seqs <= kMaxSeqsBalanced;
+  if (a.partition_size == 0) return true;
+  // the split kernel keeps a per-sequence prefix in LDS, and indexes the
+  // stream of all sequences' tiles with 32 bits: at most ceil(cap / 16)
+  // tiles per sequence
+  const int64_t cap = static_cast<int64_t>(a.max_blocks) * a.block_size;
+  const int64_t per_seq = (cap + kTile - 1) / kTile;
+  return a.num_seqs <= kMaxSeqsBalanced && a.num_seqs * per_seq <= 0x7fffffff;
 }
 
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream) {

@@ -89,9 +89,4 @@ struct MoveArgs {
 hipError_t launch_copy_blocks(const MoveArgs& m, hipStream_t stream);
 hipError_t launch_swap(const MoveArgs& m, bool out, hipStream_t stream);
 
-// Streaming-read probe over 4 KiB tiles of two buffers in the given order.
-hipError_t launch_stream_probe(const void* a, const void* b, int64_t buffer_bytes,
-                               const int32_t* order, int64_t n, void* sink,
-                               hipStream_t stream);
-
 }  // namespace pkv

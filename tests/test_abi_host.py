@@ -195,6 +195,98 @@ def test_binding_refuses_cpu_tensors():
                                    torch.zeros(2, dtype=torch.int32), 0.5)
 
 
+def _shape_error(fn, *args, **kw):
+    """The call must stop on a shape / dtype check (not on the GPU check,
+    which comes after every size check)."""
+    with pytest.raises(ValueError) as e:
+        fn(*args, **kw)
+    assert "on the GPU" not in str(e.value), str(e.value)
+    return str(e.value)
+
+
+def test_binding_checks_sizes_before_anything_else():
+    """Every size the binding passes is checked against the tensors first:
+    a tensor smaller than the sizes claim would be read or written out of
+    bounds on the GPU. These all fail on the host (CPU tensors: the GPU
+    check would come later)."""
+    import torch
+    import paged_kv_cache_113_amd as pkv
+    f32, bf16, i32, i64 = torch.float32, torch.bfloat16, torch.int32, torch.int64
+    S, Hq, Hkv, D, N, B, mp = 3, 8, 2, 128, 10, 16, 4
+    kp = torch.zeros(N, Hkv, B, D, dtype=bf16)
+    q = torch.zeros(S, Hq, D, dtype=bf16)
+    tab = torch.zeros(S, 5, dtype=i32)
+    ctx = torch.ones(S, dtype=i32)
+    out = torch.zeros(S, Hq, D, dtype=f32)
+    ml = torch.zeros(S, Hq, mp, dtype=f32)
+    to = torch.zeros(S, Hq, mp, D, dtype=f32)
+    att = pkv.paged_decode_attention
+    # correct shapes reach the GPU check
+    with pytest.raises(ValueError, match="on the GPU"):
+        att(out, q, kp, kp, tab, ctx, 0.1)
+    with pytest.raises(ValueError, match="on the GPU"):
+        att(None, q, kp, kp, tab, ctx, 0.1, 64, mp, ml, ml.clone(), to)
+    # an fp32 query on bf16 pools
+    _shape_error(att, out, q.float(), kp, kp, tab, ctx, 0.1)
+    # K and V pools that differ
+    _shape_error(att, out, q, kp, kp[:5], tab, ctx, 0.1)
+    _shape_error(att, out, q, kp, kp.half(), tab, ctx, 0.1)
+    # head size of the query against the pools
+    _shape_error(att, out, q[..., :64], kp, kp, tab, ctx, 0.1)
+    # one table row and one length per sequence
+    _shape_error(att, out, q, kp, kp, tab[:2], ctx, 0.1)
+    _shape_error(att, out, q, kp, kp, tab, ctx[:2], 0.1)
+    _shape_error(att, out, q, kp, kp, tab.long(), ctx, 0.1)
+    # output size
+    _shape_error(att, out[:2], q, kp, kp, tab, ctx, 0.1)
+    _shape_error(att, None, q, kp, kp, tab, ctx, 0.1)
+    # workspace smaller than max_partitions says
+    _shape_error(att, None, q, kp, kp, tab, ctx, 0.1, 64, mp + 1, ml, ml.clone(), to)
+    _shape_error(att, None, q, kp, kp, tab, ctx, 0.1, 64, mp, ml, ml.clone(), to[:, :, :2])
+    _shape_error(att, None, q, kp, kp, tab, ctx, 0.1, 64, mp, ml, None, to)
+    # the merge
+    red = pkv.paged_attention_reduce
+    with pytest.raises(ValueError, match="on the GPU"):
+        red(out, ml, ml.clone(), to, ctx, 64)
+    _shape_error(red, out, ml[:, :, :2], ml.clone(), to, ctx, 64)
+    _shape_error(red, out[:1], ml, ml.clone(), to, ctx, 64)
+    _shape_error(red, out, ml, ml.clone(), to, ctx[:1], 64)
+    # multi-token queries
+    var = pkv.paged_varlen_attention
+    T = 7
+    qv = torch.zeros(T, Hq, D, dtype=bf16)
+    qsl = torch.tensor([0, 2, 5, 7], dtype=i32)
+    outv = torch.zeros(T, Hq, D, dtype=f32)
+    mlv = torch.zeros(T, Hq, mp, dtype=f32)
+    tov = torch.zeros(T, Hq, mp, D, dtype=f32)
+    with pytest.raises(ValueError, match="on the GPU"):
+        var(outv, qv, kp, kp, tab, qsl, ctx, 0.1, mp, mlv, mlv.clone(), tov)
+    _shape_error(var, outv, qv, kp, kp, tab, qsl[:3], ctx, 0.1, mp, mlv, mlv.clone(), tov)
+    _shape_error(var, outv, qv, kp, kp, tab[:2], qsl, ctx, 0.1, mp, mlv, mlv.clone(), tov)
+    _shape_error(var, outv, qv, kp, kp, tab, qsl, ctx, 0.1, mp, mlv[:5], mlv.clone(), tov)
+    _shape_error(var, outv, qv, kp, kp, tab, qsl, ctx, 0.1, mp + 1, mlv, mlv.clone(), tov)
+    _shape_error(var, outv[:3], qv, kp, kp, tab, qsl, ctx, 0.1, mp, mlv, mlv.clone(), tov)
+    _shape_error(var, outv, qv.half(), kp, kp, tab, qsl, ctx, 0.1, mp, mlv, mlv.clone(), tov)
+    # the write
+    wr = pkv.paged_kv_write
+    kn = torch.zeros(S, Hkv, D, dtype=bf16)
+    sl = torch.zeros(S, dtype=i64)
+    with pytest.raises(ValueError, match="on the GPU"):
+        wr(kp, kp.clone(), kn, kn.clone(), sl)
+    _shape_error(wr, kp, kp.clone(), kn, kn.clone(), sl[:2])
+    _shape_error(wr, kp, kp.clone(), kn[:, :1], kn[:, :1].clone(), sl)
+    _shape_error(wr, kp, kp.clone(), kn.float(), kn.float(), sl)
+    _shape_error(wr, kp, kp.clone(), kn, kn.clone(), sl.int())
+    # slot mapping and the checking gather
+    _shape_error(pkv.paged_slot_mapping, sl[:2], tab, ctx, B)
+    _shape_error(pkv.paged_slot_mapping, sl, tab[:2], ctx, B)
+    ko = torch.zeros(S, Hkv, 40, D, dtype=bf16)
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.paged_kv_gather(ko, ko.clone(), kp, kp, tab, ctx)
+    _shape_error(pkv.paged_kv_gather, ko[:, :1], ko[:, :1].clone(), kp, kp, tab, ctx)
+    _shape_error(pkv.paged_kv_gather, ko, ko.clone(), kp, kp, tab[:1], ctx)
+
+
 def test_product_path_does_not_import_the_oracle():
     """The library package and the input generators never import oracle/."""
     for sub in ("paged_kv_cache_113_amd", "workloads"):
@@ -204,14 +296,3 @@ def test_product_path_does_not_import_the_oracle():
                     text = open(os.path.join(dirpath, fn)).read()
                     assert "import oracle" not in text and "from oracle" not in text, fn
                     assert "attn_ref" not in text and "liboracle" not in text, fn
-
-
-def test_stream_probe_validation(lib):
-    f = lib.pkv_stream_read_probe
-    assert f(P, P, 4095, P, 8, P, None) == ESHAPE      # not whole 4 KiB tiles
-    assert f(P, P, 0, P, 8, P, None) == ESHAPE
-    assert f(P, P, 8192, P, -1, P, None) == ESHAPE
-    assert f(P, P, 8192, P, 0, P, None) == OK          # nothing to read
-    assert f(None, P, 8192, P, 8, P, None) == ENULL
-    assert f(P, P, 8192, None, 8, P, None) == ENULL
-    assert f(P, P, 8192, P, 8, None, None) == ENULL

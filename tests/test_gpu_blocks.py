@@ -1,6 +1,6 @@
 """GPU parity of the whole-block moves: copy-on-write block copies and swap
 out / in through pinned host memory. All of it is bit-exact against the
-oracle's definitions; a fork-and-append step is checked end to end (the
+oracle's definitions (copy_blocks, swap_out, swap_in); a fork-and-append step is checked end to end (the
 oracle allocator decides copies and slots, the GPU copies and writes, every
 branch's attention matches the oracle), and a swap round trip into fresh
 blocks leaves attention bitwise unchanged."""
@@ -138,9 +138,10 @@ def test_cow_fork_step_end_to_end(dev, pkv):
 
 
 def test_swap_round_trip(dev, pkv):
-    """Swap 3 sequences' blocks out to pinned memory (bytes = the pool's
-    blocks, in order), back in to fresh blocks, rewrite their tables:
-    attention is bitwise the same as before the swap."""
+    """Swap 3 sequences' blocks out to pinned memory, back in to fresh
+    blocks, rewrite their tables: the host buffer and the restored pools are
+    bit for bit the oracle's swap_out / swap_in, and attention is bitwise the
+    same as before the swap."""
     b = W.mha_fp16(num_seqs=5, lo=20, hi=200)
     say(f"case: swap round trip, blocks {b.num_blocks}")
     L = 2
@@ -167,6 +168,10 @@ def test_swap_round_trip(dev, pkv):
     ids_t = torch.as_tensor(ids, dtype=torch.int64, device=dev)
     pkv.paged_kv_swap_out(buf, ks, vs, ids_t)
     torch.cuda.synchronize()
+    k_raw = [_raw(k, b.dtype) for k in ks]
+    v_raw = [_raw(v, b.dtype) for v in vs]
+    want_host = oracle.scatter.swap_out(k_raw, v_raw, ids)
+    assert np.array_equal(oracle._raw(buf, b.dtype), want_host)
     bits = lambda t: t.contiguous().view(torch.int16)   # noqa: E731  (NaN poison compares)
     for l in range(L):
         assert torch.equal(bits(buf[l, 0]), bits(ks[l][ids_t].cpu()))
@@ -184,7 +189,13 @@ def test_swap_round_trip(dev, pkv):
         ks[l][ids_t] = float("nan")
         vs[l][ids_t] = float("nan")
     fresh_t = torch.as_tensor(fresh, dtype=torch.int64, device=dev)
+    want_k, want_v = oracle.scatter.swap_in([_raw(k, b.dtype) for k in ks],
+                                            [_raw(v, b.dtype) for v in vs], want_host, fresh)
     pkv.paged_kv_swap_in(buf, ks, vs, fresh_t)
+    torch.cuda.synchronize()
+    for l in range(L):
+        assert np.array_equal(_raw(ks[l], b.dtype), want_k[l]), ("swap in, K", l)
+        assert np.array_equal(_raw(vs[l], b.dtype), want_v[l]), ("swap in, V", l)
     remap = dict(zip(ids, fresh))
     tab2 = b.block_table.copy()
     for s in victims:
@@ -269,7 +280,8 @@ def test_swap_full_size(dev, pkv):
     and back into a shuffle of spare and freed blocks. The pools are left
     uninitialised except for the swapped blocks (the kernels read nothing
     else); every host slab and every restored block is compared bit for bit,
-    and sampled other blocks are untouched."""
+    sampled other blocks are untouched, and layers 0 and 31 (host slabs and
+    whole pools) equal the oracle's swap_out / swap_in."""
     torch.cuda.empty_cache()
     b = W.decode_step_bf16()
     L = b.num_layers
@@ -295,6 +307,10 @@ def test_swap_full_size(dev, pkv):
             bits[ids_t] = _pattern(ids_t, l, kv, elems)
             snap.append(bits[untouched].clone())
             lst.append(t)
+    # layers 0 and 31 against the oracle, whole pools
+    ends = (0, L - 1)
+    k_end = [_raw(ks[l], "bf16") for l in ends]
+    v_end = [_raw(vs[l], "bf16") for l in ends]
     buf = torch.empty((L, 2, len(ids)) + shape[1:], dtype=torch.bfloat16, pin_memory=True)
     pools = pkv.PoolSet(ks, vs)
     pkv.paged_kv_swap_out(buf, pools, None, ids_t)
@@ -303,8 +319,16 @@ def test_swap_full_size(dev, pkv):
         for kv in (0, 1):
             got = buf[l, kv].view(torch.int16).reshape(len(ids), elems).to(dev)
             assert torch.equal(got, _pattern(ids_t, l, kv, elems)), ("out", l, kv)
+    want_host = oracle.scatter.swap_out(k_end, v_end, ids)
+    assert np.array_equal(oracle._raw(buf[list(ends)], "bf16"), want_host)
     pkv.paged_kv_swap_in(buf, pools, None, fresh_t)
     torch.cuda.synchronize()
+    want_k, want_v = oracle.scatter.swap_in(k_end, v_end, want_host, fresh)
+    del k_end, v_end
+    for j, l in enumerate(ends):
+        assert np.array_equal(_raw(ks[l], "bf16"), want_k[j]), ("oracle swap in, K", l)
+        assert np.array_equal(_raw(vs[l], "bf16"), want_v[j]), ("oracle swap in, V", l)
+    del want_k, want_v
     i = 0
     for l in range(L):
         for kv, t in ((0, ks[l]), (1, vs[l])):

@@ -4,7 +4,7 @@ Bit-exact: slot mapping, the K/V write, the block-table gather.
 Attention: max abs error <= 2e-3 against fp64 (the bar for fp16/bf16 KV with
 fp32 accumulation), unsplit and split + merge, at sizes the oracle checks
 element by element (several tiles, ragged tails) and at the full workload
-sizes on sampled sequences.
+sizes on every sequence, in the launch configurations the benchmark times.
 """
 import numpy as np
 import pytest
@@ -61,6 +61,49 @@ def test_tiny_page_example(dev, pkv):
         e = max_err(got.cpu(), want)
         say(f"  P={P}: max abs err {e:.3e}")
         assert e <= TOL
+
+
+def test_tiny_page_example_paged_equals_contiguous_bitwise(dev, pkv):
+    """The glossary page's experiment on the GPU (its plain kernel: fp32,
+    D = 8, B = 4): attention through the page tables equals attention over
+    the same histories laid out contiguously (each sequence's positions in
+    consecutive blocks of its own, identity order), max abs diff 0 as the page
+    prints; and moving the physical blocks (rewriting the tables) changes no
+    output bit either."""
+    say("case: tiny page example, paged vs contiguous, bitwise")
+    b = W.tiny_page_example()
+    t = W.layer_tensors(b, device=dev)
+    meta = device_meta(b, dev)
+    B = b.block_size
+    # contiguous layout: sequence s's position p in block base_s + p // B
+    width = b.max_blocks
+    ck = torch.zeros((b.num_seqs * width,) + tuple(t["k_cache"].shape[1:]), device=dev)
+    cv = torch.zeros_like(ck)
+    ctab = torch.full((b.num_seqs, width), -1, dtype=torch.int32)
+    for s, L in enumerate(b.context_lens):
+        for p in range(int(L)):
+            src = int(b.block_table[s][p // B])
+            ck[s * width + p // B, :, p % B] = t["k_cache"][src, :, p % B]
+            cv[s * width + p // B, :, p % B] = t["v_cache"][src, :, p % B]
+            ctab[s, p // B] = s * width + p // B
+    cmeta = dict(meta, table=ctab.to(dev))
+    perm = torch.randperm(b.num_blocks, generator=torch.Generator().manual_seed(53)).to(dev)
+    pk = torch.empty_like(t["k_cache"])
+    pv = torch.empty_like(t["v_cache"])
+    pk[perm] = t["k_cache"]
+    pv[perm] = t["v_cache"]
+    ptab = torch.where(meta["table"] >= 0, perm[meta["table"].clamp(min=0).long()].int(),
+                       meta["table"]).contiguous()
+    for P in (0, 4, 8):
+        paged = gpu_attention(pkv, b, t, meta, dev, P)
+        cont = gpu_attention(pkv, b, dict(t, k_cache=ck, v_cache=cv), cmeta, dev, P)
+        moved = gpu_attention(pkv, b, dict(t, k_cache=pk, v_cache=pv), dict(meta, table=ptab),
+                              dev, P)
+        torch.cuda.synchronize()
+        diff = float((paged - cont).abs().max())
+        say(f"  P={P}: max abs diff paged vs contiguous {diff:.3e}")
+        assert diff == 0.0 and torch.equal(paged, cont)
+        assert torch.equal(paged, moved)
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))
@@ -262,10 +305,12 @@ def test_edge_lengths(dev, pkv):
     assert torch.isfinite(got[6]).all()
 
 
+# every sequence at full size; the partition sizes include the ones the
+# benchmark times (256 for the MHA case, 1024 for the others)
 FULL = {
-    "mha_fp16": (W.mha_fp16, None, (0, 512)),
-    "gqa_shared_bf16": (W.gqa_shared_bf16, None, (0, 512)),
-    "long_split_bf16": (W.long_split_bf16, None, (512,)),
+    "mha_fp16": (W.mha_fp16, None, (0, 256, 512)),
+    "gqa_shared_bf16": (W.gqa_shared_bf16, None, (0, 512, 1024)),
+    "long_split_bf16": (W.long_split_bf16, None, (512, 1024)),
 }
 
 
@@ -290,7 +335,8 @@ def test_attention_full_size(dev, pkv, name):
 @pytest.mark.parametrize("layer", [0, 31])
 def test_decode_step_full_size_layer(dev, pkv, layer):
     """One layer of the 32-layer decode step at full size: slot mapping and
-    write bit-exact; attention (split 512, as timed) on sampled sequences."""
+    write bit-exact; attention of all 512 sequences at partition size 1024
+    (the benchmark's launch: max_partitions = ceil(max ctx / 1024)) and 512."""
     b = W.decode_step_bf16()
     say(f"case: full decode step layer {layer} S={b.num_seqs} blocks={b.num_blocks}")
     t = W.layer_tensors(b, layer=layer, device=dev)
@@ -298,19 +344,16 @@ def test_decode_step_full_size_layer(dev, pkv, layer):
     k, v, slots = oracle_pools_after_write(b, th)
     meta = device_meta(b, dev)
     got_slots = gpu_write(pkv, b, t, meta, dev)
-    out = gpu_attention(pkv, b, t, meta, dev, 512)
+    outs = {P: gpu_attention(pkv, b, t, meta, dev, P) for P in (1024, 512)}
     torch.cuda.synchronize()
     assert got_slots.cpu().tolist() == slots
     assert np.array_equal(oracle._raw(t["k_cache"].cpu(), b.dtype), k)
-    rng = np.random.default_rng(layer)
-    order = np.argsort(b.context_lens)
-    seqs = sorted(set(rng.choice(b.num_seqs, 20, replace=False).tolist() +
-                      [int(order[0]), int(order[-1])] +
-                      [int(s) for s in np.flatnonzero(b.positions % 16 == 0)[:4]]))
-    want = oracle_attention(b, th["q"], k, v, seqs)
-    e = max_err(out.cpu()[seqs], want)
-    say(f"  sampled {len(seqs)} seqs: max abs err {e:.3e}")
-    assert e <= TOL
+    assert np.array_equal(oracle._raw(t["v_cache"].cpu(), b.dtype), v)
+    want = oracle_attention(b, th["q"], k, v)
+    for P, out in outs.items():
+        e = max_err(out.cpu(), want)
+        say(f"  P={P}, all {b.num_seqs} seqs: max abs err {e:.3e}")
+        assert e <= TOL
 
 
 @pytest.mark.parametrize("name,P,mp_override", [

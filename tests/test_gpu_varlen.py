@@ -195,10 +195,9 @@ FULL = {
 
 
 @pytest.mark.parametrize("name", sorted(FULL))
-def test_varlen_full_size_sampled(dev, pkv, name):
-    """Full-size batches, in the launch configuration the benchmark times:
-    every query row of sampled sequences (the shortest, the longest, every
-    prefill chunk, random others) against the oracle."""
+def test_varlen_full_size(dev, pkv, name):
+    """Full-size batches, in the launch configuration the benchmark times
+    (max_partitions 8): every query row against the oracle."""
     b = FULL[name]()
     say(f"case: varlen full {name} S={b.num_seqs} T={b.num_tokens} blocks={b.num_blocks}")
     t = W.layer_tensors(b, device=dev)
@@ -207,12 +206,7 @@ def test_varlen_full_size_sampled(dev, pkv, name):
     torch.cuda.synchronize()
     assert torch.isfinite(got).all()
     th = host(t)
-    rng = np.random.default_rng(7)
-    order = np.argsort(b.context_lens)
-    big = np.flatnonzero(b.query_lens > 1)[:8]
-    seqs = sorted(set(rng.choice(b.num_seqs, 12, replace=False).tolist() +
-                      [int(order[0]), int(order[-1])] + [int(s) for s in big]))
-    want, rows = oracle_varlen(b, th["q"], th["k_cache"], th["v_cache"], seqs)
-    e = max_err(got.cpu()[torch.as_tensor(rows)], want)
-    say(f"  sampled {len(seqs)} seqs / {len(rows)} rows: max abs err {e:.3e}")
+    want = oracle_varlen(b, th["q"], th["k_cache"], th["v_cache"])
+    e = max_err(got.cpu(), want)
+    say(f"  all {b.num_tokens} rows: max abs err {e:.3e}")
     assert e <= TOL
