@@ -30,8 +30,10 @@
  *
  * Ownership and threading: the caller allocates and owns every buffer. The
  * library allocates nothing and keeps no pointer after a call returns. Its
- * only global state is a write-once, per-device cache of one occupancy query
- * (atomics; calls are reentrant and thread-safe). It never synchronises:
+ * global state is a write-once, per-device cache of one occupancy query and
+ * of the static scratch buffer's address (atomics; calls are reentrant and
+ * thread-safe), and that buffer itself, which only
+ * paged_varlen_attention_noalloc uses. It never synchronises:
  * each call validates its arguments on the host, then enqueues kernels on
  * `stream` (a hipStream_t passed as void*; NULL is the default stream) and
  * returns. Device faults surface at the caller's next synchronisation.
@@ -65,7 +67,8 @@ enum pkv_status {
   PKV_ERR_LAUNCH = -6,      /* the HIP runtime refused a launch */
   PKV_ERR_HOST = -7,        /* a host buffer is too small or not pinned memory */
   PKV_ERR_STATE = -8,       /* not valid in the block pool's current state */
-  PKV_ERR_CAPACITY = -9     /* not enough free blocks (nothing was taken) */
+  PKV_ERR_CAPACITY = -9,    /* not enough free blocks (nothing was taken) */
+  PKV_ERR_SCRATCH = -10     /* more partials than the static scratch buffer holds */
 };
 
 /*
@@ -238,6 +241,42 @@ int paged_varlen_attention(float* out, const void* query, const void* k_cache,
                            int max_blocks_per_seq, float scale, int max_partitions,
                            float* max_logits, float* exp_sums, float* tmp_out, int dtype,
                            void* stream);
+
+/*
+ * paged_varlen_attention_noalloc -- paged_varlen_attention for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments, meaning, kernels
+ * and results as paged_varlen_attention (bit for bit, for the same inputs
+ * and max_partitions on the same device), without the workspace: the split
+ * partials go to a buffer the library holds in static device memory,
+ * paged_varlen_attention_noalloc_limit() bytes (128 MiB) on each device it
+ * runs on, kept until the process ends. The call allocates nothing (no
+ * hipMalloc, no allocating library routine); its first call on a device
+ * looks the buffer's address up once.
+ *
+ * Limit: paged_varlen_attention_noalloc_bytes(num_tokens, num_heads,
+ * head_size, max_partitions) must not exceed the buffer, else
+ * PKV_ERR_SCRATCH (nothing enqueued). Nothing in the buffer needs to start
+ * at zero: every partial the merge reads is written by the same call first.
+ * All calls on one device share the buffer, which keeps the last call's
+ * contents: calls that overlap on one device (other streams, other host
+ * threads) race and give wrong results; serialise them (one stream, or
+ * events between streams).
+ * Errors: those of paged_varlen_attention except PKV_ERR_WORKSPACE, plus
+ * PKV_ERR_SCRATCH.
+ */
+int paged_varlen_attention_noalloc(float* out, const void* query, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_table,
+                                   const int32_t* query_start_loc, const int32_t* context_lens,
+                                   int num_seqs, int num_tokens, int num_heads, int num_kv_heads,
+                                   int head_size, int block_size, int64_t num_blocks,
+                                   int max_blocks_per_seq, float scale, int max_partitions,
+                                   int dtype, void* stream);
+/* Static scratch bytes a paged_varlen_attention_noalloc call needs (0 for
+ * non-positive arguments), and the buffer's size. Host-only. */
+size_t paged_varlen_attention_noalloc_bytes(int num_tokens, int num_heads, int head_size,
+                                            int max_partitions);
+size_t paged_varlen_attention_noalloc_limit(void);
 
 /*
  * paged_attention_workspace_bytes -- bytes of max_logits + exp_sums + tmp_out

@@ -36,6 +36,11 @@ SIGNATURES = {
                                  _I32, _P]),
     "paged_kv_swap_in": (_I32, [_P, _I64, _P, _P, _I32, _P, _I64, _I64, _I32, _I32, _I32,
                                 _I32, _P]),
+    "paged_varlen_attention_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                              _I32, _I32, _I32, _I64, _I32, _F32, _I32, _I32,
+                                              _P]),
+    "paged_varlen_attention_noalloc_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
+    "paged_varlen_attention_noalloc_limit": (ctypes.c_size_t, []),
     "paged_attention_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "paged_kv_gather": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32,
                                _I32, _I32, _P]),
@@ -224,6 +229,40 @@ def paged_varlen_attention(out, query, k_cache, v_cache, block_table, query_star
         _ptr(query_start_loc), _ptr(context_lens), context_lens.shape[0], t, hq, hkv, d, b, n,
         block_table.shape[1], float(scale), max_partitions, _ptr(max_logits), _ptr(exp_sums),
         _ptr(tmp_out), _DTYPE[query.dtype], _stream(stream)))
+
+
+def paged_varlen_attention_noalloc(out, query, k_cache, v_cache, block_table,
+                                   query_start_loc, context_lens, scale, max_partitions,
+                                   stream=None):
+    """paged_varlen_attention without a workspace: the partials go to the
+    library's static device buffer (no device allocation in the call). Calls
+    that overlap on one GPU race on that buffer."""
+    n, hkv, b, d = _pool_geometry(k_cache, v_cache)
+    _need(query.dim() == 3 and query.shape[2] == d, "query is [num_tokens, Hq, D]")
+    _need(query.dtype == k_cache.dtype, "query and pools differ in dtype")
+    t, hq, _ = query.shape
+    _i32(block_table, query_start_loc, context_lens)
+    ns = context_lens.numel()
+    _need(block_table.dim() == 2 and block_table.shape[0] == ns,
+          "block_table is [num_seqs, max_blocks]")
+    _need(query_start_loc.numel() == ns + 1, "query_start_loc has num_seqs + 1 entries")
+    _need(out.dtype == torch.float32 and out.numel() == t * hq * d,
+          "out is float32 [num_tokens, Hq, D]")
+    _dev(out, query, k_cache, v_cache, block_table, query_start_loc, context_lens)
+    _check("paged_varlen_attention_noalloc", lib.paged_varlen_attention_noalloc(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(query_start_loc), _ptr(context_lens), ns, t, hq, hkv, d, b, n,
+        block_table.shape[1], float(scale), max_partitions, _DTYPE[query.dtype],
+        _stream(stream)))
+
+
+def paged_varlen_attention_noalloc_bytes(num_tokens, num_heads, head_size, max_partitions):
+    return int(lib.paged_varlen_attention_noalloc_bytes(num_tokens, num_heads, head_size,
+                                                        max_partitions))
+
+
+def paged_varlen_attention_noalloc_limit():
+    return int(lib.paged_varlen_attention_noalloc_limit())
 
 
 class PoolSet:

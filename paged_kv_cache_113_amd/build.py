@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 SOURCES = ["api.cpp", "cache_ops.hip", "decode_fast.hip", "decode_generic.hip", "block_ops.hip",
-           "prefill.hip", "prefix_cache.cpp"]
+           "prefill.hip", "prefix_cache.cpp", "scratch.hip"]
 PROBE_SOURCE = os.path.join(HERE, "probe", "stream_probe.hip")
 PROBE_LIB = os.path.join(HERE, "libpkvprobe.so")
 ARCH = "gfx950"

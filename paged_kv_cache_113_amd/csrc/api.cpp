@@ -132,6 +132,10 @@ int varlen_launch(const pkv::DecodeArgs& a, hipStream_t stream) {
                                           a.max_partitions, stream));
 }
 
+// Bytes of one part of the static scratch, rounded up to 256 (each part
+// starts 256-byte aligned).
+size_t scratch_part(size_t floats) { return (floats * sizeof(float) + 255) & ~size_t(255); }
+
 }  // namespace
 
 extern "C" {
@@ -249,6 +253,42 @@ int paged_varlen_attention(float* out, const void* query, const void* k_cache,
   return varlen_launch(a, as_stream(stream));
 }
 
+int paged_varlen_attention_noalloc(float* out, const void* query, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_table,
+                                   const int32_t* query_start_loc, const int32_t* context_lens,
+                                   int num_seqs, int num_tokens, int num_heads, int num_kv_heads,
+                                   int head_size, int block_size, int64_t num_blocks,
+                                   int max_blocks_per_seq, float scale, int max_partitions,
+                                   int dtype, void* stream) {
+  pkv::DecodeArgs a{};
+  const int rc = varlen_args(a, out, query, k_cache, v_cache, block_table, query_start_loc,
+                             context_lens, num_seqs, num_tokens, num_heads, num_kv_heads,
+                             head_size, block_size, num_blocks, max_blocks_per_seq, scale,
+                             max_partitions, dtype);
+  if (rc != kLaunch) return rc;
+  const size_t bytes = paged_varlen_attention_noalloc_bytes(num_tokens, num_heads, head_size,
+                                                            max_partitions);
+  if (bytes == 0 || bytes > pkv::kNoAllocScratchBytes) return PKV_ERR_SCRATCH;
+  // the first HIP call: the static buffer's address on the current device
+  void* base = nullptr;
+  if (pkv::noalloc_scratch(&base) != hipSuccess) return PKV_ERR_LAUNCH;
+  const size_t ml = scratch_part(static_cast<size_t>(num_tokens) * num_heads * max_partitions);
+  char* p = static_cast<char*>(base);
+  a.max_logits = reinterpret_cast<float*>(p);
+  a.exp_sums = reinterpret_cast<float*>(p + ml);
+  a.tmp_out = reinterpret_cast<float*>(p + 2 * ml);
+  return varlen_launch(a, as_stream(stream));
+}
+
+size_t paged_varlen_attention_noalloc_bytes(int num_tokens, int num_heads, int head_size,
+                                            int max_partitions) {
+  if (num_tokens <= 0 || num_heads <= 0 || head_size <= 0 || max_partitions <= 0) return 0;
+  const size_t slots = static_cast<size_t>(num_tokens) * num_heads * max_partitions;
+  return 2 * scratch_part(slots) + scratch_part(slots * head_size);
+}
+
+size_t paged_varlen_attention_noalloc_limit(void) { return pkv::kNoAllocScratchBytes; }
+
 int paged_kv_copy_blocks(void* const* k_caches, void* const* v_caches, int num_layers,
                          const int64_t* block_mapping, int64_t num_pairs, int64_t num_blocks,
                          int num_kv_heads, int block_size, int head_size, int dtype,
@@ -320,6 +360,8 @@ const char* pkv_strerror(int code) {
     case PKV_ERR_HOST: return "the host buffer is too small or not pinned memory the GPU reaches";
     case PKV_ERR_STATE: return "not valid in the block pool's current state";
     case PKV_ERR_CAPACITY: return "not enough free blocks (nothing was taken)";
+    case PKV_ERR_SCRATCH:
+      return "the call's partials exceed the library's static scratch buffer";
     default: return "unknown pkv status code";
   }
 }

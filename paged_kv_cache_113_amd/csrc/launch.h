@@ -62,6 +62,11 @@ hipError_t launch_prefill_fast(const DecodeArgs& a, hipStream_t stream);
 // Plain path: one wave per (query row, head), output written directly.
 hipError_t launch_varlen_generic(const DecodeArgs& a, hipStream_t stream);
 
+// Static scratch of paged_varlen_attention_noalloc: its size, and its device
+// address on the current device (looked up on the first call per device).
+constexpr size_t kNoAllocScratchBytes = size_t{128} << 20;
+hipError_t noalloc_scratch(void** out);
+
 // context_lens NULL: every row takes part (multi-token queries).
 hipError_t launch_reduce(float* out, const float* max_logits, const float* exp_sums,
                          const float* tmp_out, const int32_t* context_lens, int num_seqs,

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     for n in ("paged_kv_write", "paged_decode_attention", "paged_attention_reduce",
               "paged_slot_mapping", "paged_kv_gather", "paged_attention_workspace_bytes",
               "paged_varlen_attention", "paged_kv_copy_blocks", "paged_kv_swap_out",
-              "paged_kv_swap_in", "pkv_strerror"):
+              "paged_kv_swap_in", "paged_varlen_attention_noalloc", "pkv_strerror"):
         assert n in names
 
 
@@ -117,6 +117,42 @@ def test_varlen_validation(lib):
     assert varlen(lib, to=None) == EWS
     assert varlen(lib, ml=None, dtype=0, D=64) == EWS     # required on every path
     assert varlen(lib, T=1 << 24, Hq=64, Hkv=8) == EUNSUP  # (row, head) waves beyond 2^26
+
+
+def varlen_noalloc(lib, **kw):
+    a = dict(out=P, q=P, k=P, v=P, table=P, qsl=P, ctx=P, S=2, T=9, Hq=8, Hkv=2, D=128, B=16,
+             N=10, MB=4, scale=0.1, mp=8, dtype=2)
+    a.update(kw)
+    return lib.paged_varlen_attention_noalloc(a["out"], a["q"], a["k"], a["v"], a["table"],
+                                              a["qsl"], a["ctx"], a["S"], a["T"], a["Hq"],
+                                              a["Hkv"], a["D"], a["B"], a["N"], a["MB"],
+                                              a["scale"], a["mp"], a["dtype"], None)
+
+
+ESCRATCH = -10
+
+
+def test_varlen_noalloc_validation(lib):
+    """The no-allocation variant checks what paged_varlen_attention checks,
+    and refuses partials beyond its static buffer, all before any HIP call."""
+    limit = lib.paged_varlen_attention_noalloc_limit()
+    assert limit == 128 << 20
+    need = lib.paged_varlen_attention_noalloc_bytes
+    # three parts, each rounded up to 256 bytes: m, l, then the D-float rows
+    assert need(9, 8, 128, 8) == 2 * 2304 + 9 * 8 * 8 * 128 * 4
+    assert need(1, 1, 1, 1) == 3 * 256
+    assert need(0, 8, 128, 8) == 0 and need(9, 8, 128, -1) == 0
+    assert varlen_noalloc(lib, dtype=3) == EDTYPE
+    assert varlen_noalloc(lib, Hq=6, Hkv=4) == ESHAPE
+    assert varlen_noalloc(lib, mp=0) == ESHAPE
+    assert varlen_noalloc(lib, D=300) == EUNSUP
+    assert varlen_noalloc(lib, T=0) == OK and varlen_noalloc(lib, S=0) == OK
+    assert varlen_noalloc(lib, qsl=None) == ENULL
+    assert varlen_noalloc(lib, out=None) == ENULL
+    # 2048 rows x 32 heads x 8 slots x 130 floats = 272 MB > 128 MiB
+    assert varlen_noalloc(lib, T=2048, Hq=32, Hkv=8, mp=8) == ESCRATCH
+    assert varlen_noalloc(lib, T=9, mp=1 << 20) == ESCRATCH
+    assert b"static scratch" in lib.pkv_strerror(ESCRATCH)
 
 
 EHOST = -7
