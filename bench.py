@@ -3,8 +3,11 @@
 Default workload: the full decode step -- 512 sequences, cached lengths
 U{64..4096}, 32 layers, bf16, Hq=32, Hkv=8, D=128, block 16. One step = one
 slot-mapping launch for the batch, then for every layer: the new tokens' K/V
-write, split decode attention (balanced pieces, 1024-position slots) and the
-log-sum-exp merge. Inputs are resident in HBM before timing starts.
+write, and split decode attention (balanced pieces, 1024-position slots) with
+its log-sum-exp merge in the same launch (paged_decode_attention_merged;
+``--merge two-launch`` runs the split call and paged_attention_reduce
+instead, as the single-layer workloads do by default).
+Inputs are resident in HBM before timing starts.
 
 Multi-token workloads (``--workload spec_verify_bf16`` / ``mixed_prefill_bf16``):
 one step is one paged_varlen_attention call (balanced split kernel over
@@ -525,6 +528,13 @@ def main():
                          "define 16, or 32 for the long split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--merge", choices=["auto", "one-launch", "two-launch"], default="auto",
+                    help="split decode and its merge: paged_decode_attention_merged (one launch) "
+                         "or paged_decode_attention + paged_attention_reduce (two); auto takes "
+                         "the faster on MI355X: one launch for the 32-layer decode step (most of "
+                         "its sequences finish in one piece), two for the single-layer cases "
+                         "(many pieces per sequence: the in-kernel merge lengthens the kernel's "
+                         "tail by about what the second launch costs)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured in a HIP graph (per-kernel times "
                          "still come from eager steps)")
@@ -533,6 +543,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    args.two_call = args.merge == "two-launch" or (
+        args.merge == "auto" and args.workload != "decode_step_bf16")
     if args.steps is None:
         args.steps = 10 if args.workload == "decode_step_bf16" else 20
 
@@ -593,6 +605,8 @@ def main():
         ml = torch.empty(ws_shape, device=dev)
         es = torch.empty(ws_shape, device=dev)
         to = torch.empty(ws_shape + (batch.head_size,), device=dev)
+    # arrival counters of the merged call: zeroed once, left zero by each call
+    counters = torch.zeros(batch.num_seqs * batch.num_kv_heads, dtype=torch.int32, device=dev)
     flush = None
     if args.workload != "decode_step_bf16":
         # 1 GiB, written once here; each step only reads it, so the eviction
@@ -625,6 +639,10 @@ def main():
                 timed("decode", record, lambda: pkv.paged_varlen_attention(
                     outs[l], t["q"], t["k_cache"], t["v_cache"], table, qsl, ctx, scale, mp, ml,
                     es, to))
+            elif P > 0 and not args.two_call:
+                timed("decode", record, lambda: pkv.paged_decode_attention_merged(
+                    outs[l], t["q"], t["k_cache"], t["v_cache"], table, ctx, scale, P, mp, ml,
+                    es, to, counters))
             elif P > 0:
                 timed("decode", record, lambda: pkv.paged_decode_attention(
                     None, t["q"], t["k_cache"], t["v_cache"], table, ctx, scale, P, mp, ml, es,
@@ -784,7 +802,10 @@ def main():
                      "traffic": traffic,
                      "kernel": "paged_varlen_attention (split kernel, prefill kernel, merge)"
                      if varlen
-                     else "decode_split_kernel" if P > 0 else "decode_whole_kernel",
+                     else "decode_split_kernel" + ("" if args.two_call else
+                                                   " (paged_decode_attention_merged: pieces "
+                                                   "merged in the same launch)")
+                     if P > 0 else "decode_whole_kernel",
                      "bytes_per_launch": layer_bytes,
                      "logical_bytes_per_launch": logical_bytes,
                      "read_probe": None if probe is None else {

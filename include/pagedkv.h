@@ -172,6 +172,36 @@ int paged_decode_attention(float* out, const void* query, const void* k_cache,
                            float* exp_sums, float* tmp_out, int dtype, void* stream);
 
 /*
+ * paged_decode_attention_merged -- split decode and its merge in one call.
+ *
+ * out [num_seqs, num_heads, head_size] = the result of paged_decode_attention
+ * in split mode followed by paged_attention_reduce (the "V2" partitions and
+ * their reduce kernel, source-walkthrough page, section 1.8). On the fast
+ * path this is one launch: the pieces go to the workspace as in split mode,
+ * the wave that delivers the last piece of a (sequence, KV head) merges that
+ * sequence's pieces for the KV head into out, and a sequence done in one
+ * piece writes out directly; elsewhere it is the plain split kernel and the
+ * merge kernel. Arguments as paged_decode_attention in split mode
+ * (partition_size > 0, the workspace required; its contents are unspecified
+ * afterwards), plus
+ *   counters: device int32 [num_seqs * num_kv_heads] arrival counts, all
+ *   zero before the call; the call leaves them zero again (each merging
+ *   wave resets its own), so a buffer zeroed once serves every later call.
+ * Calls that overlap must not share counters or workspace. ctx_s == 0 gives
+ * out = 0.
+ * Errors: those of paged_decode_attention, PKV_ERR_SHAPE for partition_size
+ * < 1, PKV_ERR_NULL for a NULL out, PKV_ERR_WORKSPACE for NULL counters.
+ */
+int paged_decode_attention_merged(float* out, const void* query, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* context_lens, int num_seqs, int num_heads,
+                                  int num_kv_heads, int head_size, int block_size,
+                                  int64_t num_blocks, int max_blocks_per_seq, float scale,
+                                  int partition_size, int max_partitions, float* max_logits,
+                                  float* exp_sums, float* tmp_out, int32_t* counters, int dtype,
+                                  void* stream);
+
+/*
  * paged_attention_reduce -- merge split partials into the final output.
  *
  * For each (s, h) with ctx_s >= 1, over the slots p < max_partitions with

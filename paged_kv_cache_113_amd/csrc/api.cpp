@@ -78,6 +78,50 @@ int swap_common(void* host, int64_t host_bytes, void* const* k_caches, void* con
 // else the status to return (PKV_OK for an empty call).
 constexpr int kLaunch = 1;
 
+// paged_decode_attention's argument checks (all before any HIP call); fills
+// `a`. Returns kLaunch when there is work to launch, else the status.
+int decode_args(pkv::DecodeArgs& a, float* out, const void* query, const void* k_cache,
+                const void* v_cache, const int32_t* block_table, const int32_t* context_lens,
+                int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+                int64_t num_blocks, int max_blocks_per_seq, float scale, int partition_size,
+                int max_partitions, float* max_logits, float* exp_sums, float* tmp_out,
+                int dtype) {
+  if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_size < 1 || block_size < 1 ||
+      num_blocks < 1 || max_blocks_per_seq < 1 || partition_size < 0)
+    return PKV_ERR_SHAPE;
+  if (num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  const bool split = partition_size > 0;
+  if (split && (partition_size % block_size != 0 || max_partitions < 1)) return PKV_ERR_SHAPE;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > 0x7fffffff) return PKV_ERR_SHAPE;
+  if (head_size > 256) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!query || !k_cache || !v_cache || !block_table || !context_lens) return PKV_ERR_NULL;
+  if (!split && !out) return PKV_ERR_NULL;
+  if (split && (!max_logits || !exp_sums || !tmp_out)) return PKV_ERR_WORKSPACE;
+  a.out = out;
+  a.query = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = head_size;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.scale = scale;
+  a.partition_size = partition_size;
+  a.max_partitions = split ? max_partitions : 1;
+  a.max_logits = max_logits;
+  a.exp_sums = exp_sums;
+  a.tmp_out = tmp_out;
+  a.dtype = dtype;
+  return kLaunch;
+}
+
 int varlen_args(pkv::DecodeArgs& a, float* out, const void* query, const void* k_cache,
                 const void* v_cache, const int32_t* block_table,
                 const int32_t* query_start_loc, const int32_t* context_lens, int num_seqs,
@@ -175,45 +219,47 @@ int paged_decode_attention(float* out, const void* query, const void* k_cache,
                            int max_blocks_per_seq, float scale, int partition_size,
                            int max_partitions, float* max_logits, float* exp_sums,
                            float* tmp_out, int dtype, void* stream) {
-  if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
-  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_size < 1 || block_size < 1 ||
-      num_blocks < 1 || max_blocks_per_seq < 1 || partition_size < 0)
-    return PKV_ERR_SHAPE;
-  if (num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
-  const bool split = partition_size > 0;
-  if (split && (partition_size % block_size != 0 || max_partitions < 1)) return PKV_ERR_SHAPE;
-  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > 0x7fffffff) return PKV_ERR_SHAPE;
-  if (head_size > 256) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PKV_OK;
-  if (!query || !k_cache || !v_cache || !block_table || !context_lens) return PKV_ERR_NULL;
-  if (!split && !out) return PKV_ERR_NULL;
-  if (split && (!max_logits || !exp_sums || !tmp_out)) return PKV_ERR_WORKSPACE;
-
   pkv::DecodeArgs a{};
-  a.out = out;
-  a.query = query;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_table = block_table;
-  a.context_lens = context_lens;
-  a.num_seqs = num_seqs;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_size = head_size;
-  a.block_size = block_size;
-  a.num_blocks = num_blocks;
-  a.max_blocks = max_blocks_per_seq;
-  a.scale = scale;
-  a.partition_size = partition_size;
-  a.max_partitions = split ? max_partitions : 1;
-  a.max_logits = max_logits;
-  a.exp_sums = exp_sums;
-  a.tmp_out = tmp_out;
-  a.dtype = dtype;
+  const int rc = decode_args(a, out, query, k_cache, v_cache, block_table, context_lens,
+                             num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                             num_blocks, max_blocks_per_seq, scale, partition_size,
+                             max_partitions, max_logits, exp_sums, tmp_out, dtype);
+  if (rc != kLaunch) return rc;
   if (pkv::fast_decode_supported(a))
     return launch_status(pkv::launch_decode_fast(a, as_stream(stream)));
   if (num_seqs > kMaxGridYZ || num_heads > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
   return launch_status(pkv::launch_decode_generic(a, as_stream(stream)));
+}
+
+int paged_decode_attention_merged(float* out, const void* query, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* context_lens, int num_seqs, int num_heads,
+                                  int num_kv_heads, int head_size, int block_size,
+                                  int64_t num_blocks, int max_blocks_per_seq, float scale,
+                                  int partition_size, int max_partitions, float* max_logits,
+                                  float* exp_sums, float* tmp_out, int32_t* counters, int dtype,
+                                  void* stream) {
+  if (partition_size < 1) return PKV_ERR_SHAPE;
+  pkv::DecodeArgs a{};
+  const int rc = decode_args(a, out, query, k_cache, v_cache, block_table, context_lens,
+                             num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                             num_blocks, max_blocks_per_seq, scale, partition_size,
+                             max_partitions, max_logits, exp_sums, tmp_out, dtype);
+  if (rc != kLaunch) return rc;
+  if (!out) return PKV_ERR_NULL;
+  if (!counters) return PKV_ERR_WORKSPACE;
+  if (pkv::fast_decode_supported(a)) {
+    a.counters = counters;
+    return launch_status(pkv::launch_decode_fast(a, as_stream(stream)));
+  }
+  // the plain kernel writes partials; the merge follows as a second launch
+  if (num_seqs > kMaxGridYZ || num_heads > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  a.out = nullptr;
+  hipError_t e = pkv::launch_decode_generic(a, as_stream(stream));
+  if (e != hipSuccess) return PKV_ERR_LAUNCH;
+  return launch_status(pkv::launch_reduce(out, max_logits, exp_sums, tmp_out, context_lens,
+                                          num_seqs, num_heads, head_size, partition_size,
+                                          max_partitions, as_stream(stream)));
 }
 
 int paged_attention_reduce(float* out, const float* max_logits, const float* exp_sums,

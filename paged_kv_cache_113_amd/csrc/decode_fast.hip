@@ -227,6 +227,178 @@ struct Cursor {
   int q0, qn;  // first query row of s and its query tokens (kVar)
 };
 
+// The merge of one (sequence, KV head) from its n > 1 pieces in the
+// workspace, by one wave: rows s*Hq + kvh*G + r for r < G, slots p < n. Two
+// rows per pass (one per 32-lane half), four dims of the row per lane:
+//   M = max_p m_p, w_p = l_p e^{m_p - M}, out = sum_p w_p o_p / sum_p w_p
+// (the log-sum-exp merge of paged_attention_reduce, summed in slot order).
+// The pieces are read with device-scope loads (they may come from other
+// XCDs), whose latency is long: lane q of a half holds (m, l) of slot
+// c0 + q, and each batch of eight slots' rows is loaded before any is used.
+__device__ __forceinline__ float half_max(float v) {
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 32));
+  return v;
+}
+__device__ __forceinline__ float half_sum(float v) {
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off, 32);
+  return v;
+}
+
+__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int s, int kvh, int G, int mp,
+                                             int n) {
+  constexpr int kBatch = 8;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int q = lane & 31;
+  for (int r0 = 0; r0 < G; r0 += 2) {
+    // with an odd G the second half repeats the last row and stores nothing
+    const int r = r0 + half < G ? r0 + half : G - 1;
+    const int64_t row = static_cast<int64_t>(s) * a.num_heads + kvh * G + r;
+    const float* m = a.max_logits + row * mp;
+    const float* l = a.exp_sums + row * mp;
+    const float* o = a.tmp_out + row * mp * kD + 4 * q;
+    if (n <= kBatch) {
+      // the common case: every load of the row in flight at once
+      const int pq = q < n ? q : n - 1;
+      const float mq = load_device(m + pq);
+      const float lq = load_device(l + pq);
+      float4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float* op = o + static_cast<int64_t>(u < n ? u : n - 1) * kD;
+        v[u] = make_float4(load_device(op), load_device(op + 1), load_device(op + 2),
+                           load_device(op + 3));
+      }
+      const bool ok = q < n && lq > 0.f;
+      const float Mh = half_max(ok ? mq : -INFINITY);
+      const float w = ok ? lq * expf(mq - Mh) : 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float wu = __shfl(w, (half << 5) + u, 64);
+        if (u < n && wu != 0.f) {
+          acc.x = fmaf(wu, v[u].x, acc.x);
+          acc.y = fmaf(wu, v[u].y, acc.y);
+          acc.z = fmaf(wu, v[u].z, acc.z);
+          acc.w = fmaf(wu, v[u].w, acc.w);
+        }
+      }
+      const float den = half_sum(w);
+      if (r0 + half < G)
+        *reinterpret_cast<float4*>(a.out + row * kD + 4 * q) =
+            den > 0.f ? make_float4(acc.x / den, acc.y / den, acc.z / den, acc.w / den)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      continue;
+    }
+    // (m, l) of slot c0 + q, chunk by chunk; the first chunk is kept
+    float m0 = -INFINITY, l0 = 0.f;
+    float M = -INFINITY;
+    for (int c0 = 0; c0 < n; c0 += 32) {
+      const int p = c0 + q < n ? c0 + q : n - 1;
+      const float mq = load_device(m + p);
+      const float lq = load_device(l + p);
+      const bool ok = c0 + q < n && lq > 0.f;
+      if (ok) M = fmaxf(M, mq);
+      if (c0 == 0) {
+        m0 = ok ? mq : -INFINITY;
+        l0 = ok ? lq : 0.f;
+      }
+    }
+    M = half_max(M);
+    float den = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c0 = 0; c0 < n; c0 += 32) {
+      float mq = m0, lq = l0;
+      if (c0 > 0) {
+        const int p = c0 + q < n ? c0 + q : n - 1;
+        mq = load_device(m + p);
+        lq = load_device(l + p);
+        if (!(c0 + q < n && lq > 0.f)) {
+          mq = -INFINITY;
+          lq = 0.f;
+        }
+      }
+      const float w = lq > 0.f ? lq * expf(mq - M) : 0.f;
+      den += w;
+      const int cn = n - c0 < 32 ? n - c0 : 32;
+      for (int b = 0; b < cn; b += kBatch) {
+        float4 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int p = c0 + b + u < n ? c0 + b + u : n - 1;
+          const float* op = o + static_cast<int64_t>(p) * kD;
+          v[u] = make_float4(load_device(op), load_device(op + 1), load_device(op + 2),
+                             load_device(op + 3));
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const float wu = __shfl(w, (half << 5) + ((b + u) & 31), 64);
+          if (b + u < cn && wu != 0.f) {
+            acc.x = fmaf(wu, v[u].x, acc.x);
+            acc.y = fmaf(wu, v[u].y, acc.y);
+            acc.z = fmaf(wu, v[u].z, acc.z);
+            acc.w = fmaf(wu, v[u].w, acc.w);
+          }
+        }
+      }
+    }
+    den = half_sum(den);
+    if (r0 + half < G)
+      *reinterpret_cast<float4*>(a.out + row * kD + 4 * q) =
+          den > 0.f ? make_float4(acc.x / den, acc.y / den, acc.z / den, acc.w / den)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// After a wave has written all its pieces: every sequence its range
+// [b0, b1) of the stream touched got one piece from it. For each such
+// sequence cut into n > 1 pieces, count the arrival; the wave whose arrival
+// is the n-th merges the sequence's pieces for its KV head and sets the
+// counter back to 0 for the next call. Pieces are stored at device scope
+// (written through the XCD's cache) and the wave waits for its stores
+// before it counts; the merging wave reads them with device-scope loads
+// after its count, so it sees every piece whichever XCD wrote it. (A cache
+// write-back and invalidate per wave instead cost more than the merge
+// saves.)
+template <typename RangeOf>
+__device__ __forceinline__ void merge_arrivals(const DecodeArgs& a, const int* s_pre, int S,
+                                               int lo, int b0, int b1, int kvh, int G, int mp,
+                                               RangeOf range_of) {
+  const int lane = threadIdx.x & 63;
+  auto pre = [&](int s) { return __builtin_amdgcn_readfirstlane(s_pre[s]); };
+  // the pieces' stores were issued as instructions the compiler does not
+  // track: wait for all of them explicitly
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the range's sequences, 64 at a time: lane i counts the arrival for
+  // sequence s0 + i (all counts in flight together), then the wave merges
+  // the sequences whose count it completed
+  for (int s0 = lo; s0 < S && pre(s0) < b1; s0 += 64) {
+    const int s = s0 + lane;
+    bool last = false;
+    int n = 0;
+    if (s < S) {
+      const int t0 = s_pre[s], t1 = s_pre[s + 1];
+      if (t0 < b1 && t1 > b0 && t1 > t0) {
+        n = range_of(t1 - 1) - range_of(t0) + 1;
+        if (n > 1) {
+          int32_t* ctr = a.counters + static_cast<int64_t>(s) * a.num_kv_heads + kvh;
+          last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 n - 1;
+          if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    uint64_t mine = __ballot(last);
+    while (mine) {
+      const int i = static_cast<int>(__builtin_ctzll(mine));
+      mine &= mine - 1;
+      merge_pieces(a, s0 + i, kvh, G, mp, __shfl(n, i, 64));
+    }
+  }
+}
+
 template <typename T, bool kVar>
 __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs a,
                                                                      int waves_per_kv,
@@ -247,6 +419,9 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   const int mp = a.max_partitions;
   const int cap = a.max_blocks * a.block_size;
   const int tpg = kVar ? kTile / G : 1;  // query tokens per column group
+  // decode merged in this launch: pieces still go to the workspace, the wave
+  // that delivers a sequence's last piece (per KV head) merges them into out
+  const bool fused = !kVar && a.counters != nullptr;
 
   auto seq_ctx = [&](int s) {
     int c = read_only(a.context_lens + s);
@@ -334,6 +509,16 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
       }
     }
     if (tid == 0) s_pre[S] = T1;
+  }
+  if (fused && blockIdx.x == 0) {
+    // sequences without positions get out = 0 (no piece will merge them)
+    for (int i = 0; i < per; ++i) {
+      const int s = s_lo + i;
+      if (s < S && seq_ctx(s) <= 0) {
+        float4* o = reinterpret_cast<float4*>(a.out + static_cast<int64_t>(s) * a.num_heads * kD);
+        for (int x = 0; x < a.num_heads * kD / 4; ++x) o[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
   }
   __syncthreads();
   if (T1 == 0) return;
@@ -537,21 +722,27 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
             const f32x4 v = *(const PKV_LDS f32x4*)(rec + 16 + r * (kD * 4) + ch * 16);
             float* dst = single ? a.out + row_index(sq, cg, r) * kD
                                 : a.tmp_out + (row_index(sq, cg, r) * mp + pc) * kD;
-            store_untracked(dst + ch * 4, make_float4(v[0], v[1], v[2], v[3]));
+            if (fused && !single)
+              store_untracked_device(dst + ch * 4, make_float4(v[0], v[1], v[2], v[3]));
+            else
+              store_untracked(dst + ch * 4, make_float4(v[0], v[1], v[2], v[3]));
           }
         }
         if (lane < nl) {
           const f32x2 ml = *(const PKV_LDS f32x2*)(rec + 16 + nl * (kD * 4) + lane * 8);
           const int64_t e = row_index(sq, cg, lane) * mp + pc;
           if (single) {
-            store_untracked(a.exp_sums + e, -1.f);
+            if (kVar) store_untracked(a.exp_sums + e, -1.f);
+          } else if (fused) {
+            store_untracked_device(a.max_logits + e, ml[0]);
+            store_untracked_device(a.exp_sums + e, ml[1]);
           } else {
             store_untracked(a.max_logits + e, ml[0]);
             store_untracked(a.exp_sums + e, ml[1]);
           }
         }
       }
-      if (mark && !single) mark_rest(sq, cg, pc, nl);
+      if (mark && !single && !fused) mark_rest(sq, cg, pc, nl);
       off += rec_bytes(nl);
     }
     st_used = 0;
@@ -564,7 +755,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     const int sq = kVar ? c.q0 : c.s;
     const int cg = kVar ? c.c : 0;
     const bool last = c.t == c.n - 1;
-    const bool single = kVar && last && piece == 0;
+    const bool single = (kVar || fused) && last && piece == 0;
     const int need = rec_bytes(nl);
     if (st_used + need > stage_bytes) flush();
     if (need <= stage_bytes) {
@@ -590,21 +781,28 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
                              : a.tmp_out + (row_index(sq, cg, col) * mp + piece) * kD) +
                      4 * grp;
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
-          store_untracked(dst + 16 * db,
-                          make_float4(st.acc[db][0] * inv, st.acc[db][1] * inv,
-                                      st.acc[db][2] * inv, st.acc[db][3] * inv));
+        for (int db = 0; db < 8; ++db) {
+          const float4 x = make_float4(st.acc[db][0] * inv, st.acc[db][1] * inv,
+                                       st.acc[db][2] * inv, st.acc[db][3] * inv);
+          if (fused && !single)
+            store_untracked_device(dst + 16 * db, x);
+          else
+            store_untracked(dst + 16 * db, x);
+        }
         if (grp == 0) {
           const int64_t e = row_index(sq, cg, col) * mp + piece;
           if (single) {
-            store_untracked(a.exp_sums + e, -1.f);
+            if (kVar) store_untracked(a.exp_sums + e, -1.f);
+          } else if (fused) {
+            store_untracked_device(a.max_logits + e, st.m_run * kLn2);
+            store_untracked_device(a.exp_sums + e, l_col);
           } else {
             store_untracked(a.max_logits + e, st.m_run * kLn2);
             store_untracked(a.exp_sums + e, l_col);
           }
         }
       }
-      if (last && !single) mark_rest(sq, cg, piece, nl);
+      if (last && !single && !fused) mark_rest(sq, cg, piece, nl);
     }
     st.reset();
     piece = 0;
@@ -648,6 +846,9 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     if (!step(tb, gb, ta, ga)) break;
   }
   flush();
+  if (fused) merge_arrivals(a, s_pre, S, lo, b0, b0 + len, kvh, G, mp, [&](int x) {
+      return range_of(x);
+    });
 }
 
 // Launch shapes of the split kernel on one device. The kernel is

@@ -81,6 +81,22 @@ __device__ __forceinline__ void store_untracked(float* p, float4 v) {
 __device__ __forceinline__ void store_untracked(float* p, float v) {
   asm volatile("global_store_dword %0, %1, off\n\ts_nop 1" : : "v"(p), "v"(v));
 }
+// The same stores at device scope (sc1): written through to the memory side,
+// where waves of the other XCDs read them with device-scope loads, once the
+// issuing wave has waited for them (s_waitcnt vmcnt(0)).
+__device__ __forceinline__ void store_untracked_device(float* p, float4 v) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  const f32x4_t x = {v.x, v.y, v.z, v.w};
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(x));
+}
+__device__ __forceinline__ void store_untracked_device(float* p, float v) {
+  asm volatile("global_store_dword %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(v));
+}
+// A device-scope load (reads the value at the memory side, past any copy the
+// XCD's own cache may hold).
+__device__ __forceinline__ float load_device(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Physical block of logical position `pos`, or -1 when the table row does not
 // cover it or holds an id outside [0, num_blocks). Callers skip such

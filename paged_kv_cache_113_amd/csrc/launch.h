@@ -43,6 +43,9 @@ struct DecodeArgs {
   // multi-token queries: [num_seqs + 1] query row starts, NULL for decode
   const int32_t* query_start_loc;
   int num_tokens;      // query rows (multi-token queries)
+  // split decode merged in the same launch: [num_seqs * num_kv_heads]
+  // arrival counters, zero on entry and left zero; NULL otherwise
+  int32_t* counters;
 };
 
 // Matrix-core path: f16/bf16, head_size 128, block_size % 16 == 0, G <= 16.

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     for n in ("paged_kv_write", "paged_decode_attention", "paged_attention_reduce",
               "paged_slot_mapping", "paged_kv_gather", "paged_attention_workspace_bytes",
               "paged_varlen_attention", "paged_kv_copy_blocks", "paged_kv_swap_out",
-              "paged_kv_swap_in", "paged_varlen_attention_noalloc", "pkv_strerror"):
+              "paged_kv_swap_in", "paged_varlen_attention_noalloc",
+              "paged_decode_attention_merged", "pkv_strerror"):
         assert n in names
 
 
@@ -153,6 +154,29 @@ def test_varlen_noalloc_validation(lib):
     assert varlen_noalloc(lib, T=2048, Hq=32, Hkv=8, mp=8) == ESCRATCH
     assert varlen_noalloc(lib, T=9, mp=1 << 20) == ESCRATCH
     assert b"static scratch" in lib.pkv_strerror(ESCRATCH)
+
+
+def test_merged_validation(lib):
+    """The merged call checks what the split call checks, plus out and the
+    counters, all before any HIP call."""
+    def merged(**kw):
+        a = dict(out=P, q=P, k=P, v=P, table=P, ctx=P, S=2, Hq=8, Hkv=2, D=128, B=16, N=10,
+                 MB=4, scale=0.1, P=16, mp=4, ml=P, es=P, to=P, ctr=P, dtype=2)
+        a.update(kw)
+        return lib.paged_decode_attention_merged(
+            a["out"], a["q"], a["k"], a["v"], a["table"], a["ctx"], a["S"], a["Hq"], a["Hkv"],
+            a["D"], a["B"], a["N"], a["MB"], a["scale"], a["P"], a["mp"], a["ml"], a["es"],
+            a["to"], a["ctr"], a["dtype"], None)
+    assert merged(P=0) == ESHAPE
+    assert merged(P=8) == ESHAPE                      # not a multiple of the block size
+    assert merged(mp=0) == ESHAPE
+    assert merged(dtype=5) == EDTYPE
+    assert merged(D=300) == EUNSUP
+    assert merged(S=0) == OK
+    assert merged(out=None) == ENULL
+    assert merged(ctr=None) == EWS
+    assert merged(to=None) == EWS
+    assert merged(q=None) == ENULL
 
 
 EHOST = -7

@@ -435,3 +435,114 @@ def test_split_many_pieces_per_wave(dev, pkv, name):
     e = max_err(out.cpu(), want)
     say(f"  max abs err {e:.3e}")
     assert e <= TOL
+
+
+# -- split decode and its merge in one call ------------------------------------
+
+MERGED = {
+    "tiny": (W.tiny_page_example, 4),
+    "mha_fp16": (SMALL["mha_fp16"], 64),
+    "gqa_shared_bf16": (SMALL["gqa_shared_bf16"], 64),
+    "long_split_bf16": (SMALL["long_split_bf16"], 512),
+    "decode_step_bf16": (SMALL["decode_step_bf16"], 16),
+    "gqa16_bf16": (SMALL["gqa16_bf16"], 64),
+    "gqa3_bf16": (SMALL["gqa3_bf16"], 16),
+    "plain_bf16_d96": (SMALL["plain_bf16_d96"], 8),
+    "short_gqa4_s4000": (MANY["short_gqa4_s4000"], 16),
+    "short_gqa16_s8192": (MANY["short_gqa16_s8192"], 16),
+    "full_mha_fp16": (W.mha_fp16, 256),
+    "full_gqa_shared_bf16": (W.gqa_shared_bf16, 1024),
+    "full_long_split_bf16": (W.long_split_bf16, 1024),
+}
+
+
+def _merged(pkv, b, t, meta, dev, P, mp, counters):
+    out = torch.full((b.num_seqs, b.num_heads, b.head_size), float("nan"), device=dev)
+    shape = (b.num_seqs, b.num_heads, mp)
+    ml = torch.full(shape, float("nan"), device=dev)
+    es = torch.full(shape, float("nan"), device=dev)
+    to = torch.full(shape + (b.head_size,), float("nan"), device=dev)
+    pkv.paged_decode_attention_merged(out, t["q"], t["k_cache"], t["v_cache"], meta["table"],
+                                      meta["ctx"], scale_of(b), P, mp, ml, es, to, counters)
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(MERGED))
+def test_merged_call(dev, pkv, name):
+    """paged_decode_attention_merged against the oracle (2e-3) and against
+    the split call + paged_attention_reduce (1e-5: the same partials, merged
+    in another order); twice in a row on the same counters, which it leaves
+    at zero, with bit-equal outputs."""
+    make, P = MERGED[name]
+    b = make()
+    mp = b.max_partitions(P)
+    say(f"case: merged {name} S={b.num_seqs} P={P} mp={mp}")
+    t = W.layer_tensors(b, device=dev)
+    meta = device_meta(b, dev)
+    th = host(t)
+    if b.positions is not None:
+        k, v, _ = oracle_pools_after_write(b, th)
+        gpu_write(pkv, b, t, meta, dev)
+    else:
+        k, v = th["k_cache"], th["v_cache"]
+    counters = torch.zeros(b.num_seqs * b.num_kv_heads, dtype=torch.int32, device=dev)
+    first = _merged(pkv, b, t, meta, dev, P, mp, counters)
+    second = _merged(pkv, b, t, meta, dev, P, mp, counters)
+    two = gpu_attention(pkv, b, t, meta, dev, P, mp)
+    torch.cuda.synchronize()
+    assert int(counters.abs().sum()) == 0, "counters not re-armed"
+    assert torch.equal(first, second)
+    want = oracle_attention(b, th["q"], k, v)
+    e = max_err(first.cpu(), want)
+    d = float((first - two).abs().max())
+    say(f"  max abs err {e:.3e}, vs split + merge {d:.3e}")
+    assert e <= TOL and d <= 1e-5
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_merged_decode_step_full_size(dev, pkv, layer):
+    """The benchmark's call on a whole layer of the 32-layer decode step
+    (512 sequences, partition size 1024), after the write: every sequence
+    against the oracle."""
+    b = W.decode_step_bf16()
+    say(f"case: merged full decode step layer {layer}")
+    t = W.layer_tensors(b, layer=layer, device=dev)
+    th = host(t)
+    k, v, _ = oracle_pools_after_write(b, th)
+    meta = device_meta(b, dev)
+    gpu_write(pkv, b, t, meta, dev)
+    counters = torch.zeros(b.num_seqs * b.num_kv_heads, dtype=torch.int32, device=dev)
+    out = _merged(pkv, b, t, meta, dev, 1024, b.max_partitions(1024), counters)
+    torch.cuda.synchronize()
+    assert int(counters.abs().sum()) == 0
+    e = max_err(out.cpu(), oracle_attention(b, th["q"], k, v))
+    say(f"  all {b.num_seqs} seqs: max abs err {e:.3e}")
+    assert e <= TOL
+
+
+def test_merged_edge_lengths(dev, pkv):
+    """ctx = 0 rows come out zero, ctx = 1 rows equal v_0, with one and two
+    slots per row."""
+    lens = [0, 1, 15, 16, 17, 33, 257, 0]
+    b = W.Batch(name="edges", dtype="bf16", num_heads=8, num_kv_heads=2, head_size=128,
+                block_size=16, num_blocks=64, block_table=np.full((8, 20), -1, np.int32),
+                context_lens=np.array(lens, np.int32), free_order=np.arange(64, dtype=np.int32),
+                seed=4243)
+    tab, _ = W.deal_tables(lens, 16, np.random.default_rng(2).permutation(64), width=20)
+    b.block_table = tab
+    say("case: merged edge lengths")
+    t = W.layer_tensors(b, device=dev)
+    th = host(t)
+    want = oracle_attention(b, th["q"], th["k_cache"], th["v_cache"])
+    meta = device_meta(b, dev)
+    counters = torch.zeros(8 * 2, dtype=torch.int32, device=dev)
+    for P, mp in ((16, 17), (16, 2), (64, 1)):
+        got = _merged(pkv, b, t, meta, dev, P, mp, counters)
+        torch.cuda.synchronize()
+        e = max_err(got.cpu(), want)
+        say(f"  P={P} mp={mp}: max abs err {e:.3e}")
+        assert e <= TOL
+        assert (got[0] == 0).all() and (got[7] == 0).all()
+        kv1 = th["v_cache"][int(b.block_table[1, 0]), :, 0]
+        assert torch.equal(got[1].cpu(), kv1.float().repeat_interleave(4, 0))
+        assert int(counters.abs().sum()) == 0
