@@ -399,10 +399,25 @@ __device__ __forceinline__ void merge_arrivals(const DecodeArgs& a, const int* s
   }
 }
 
+// Blocks shared by several sequences (a common prompt prefix, the branches
+// of a forked sequence: glossary page, shared prefix; nxmr.cn article,
+// section 4) sit at the same logical index of each sharer's table. The
+// split kernel finds them in its prologue by the sequences' first blocks (a
+// hash in LDS): for each first block held by more than one sequence, the
+// shared run is the leading blocks the lowest-numbered holder and another
+// holder have in common. Before the stream starts, the workgroups of each
+// XCD read every line of those runs once with plain loads, so that the lines
+// sit in that XCD's cache when the sharers' non-temporal stream reaches them.
+constexpr int kShareSlotBytes = 16;   // hash slot: key / run, lowest holder, count, another
+__device__ __forceinline__ uint32_t share_hash(int32_t b, int bits) {
+  return (static_cast<uint32_t>(b) * 2654435761u) >> (32 - bits);
+}
+
 template <typename T, bool kVar>
 __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs a,
                                                                      int waves_per_kv,
-                                                                     int stage_bytes) {
+                                                                     int stage_bytes,
+                                                                     int share_bits) {
   // dynamic LDS: the tile prefix [S + 1], then one staging area of
   // stage_bytes per wave for finished pieces
   extern __shared__ __attribute__((aligned(16))) int s_pre[];  // [S + 1]: tiles before sequence s
@@ -521,6 +536,100 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     }
   }
   __syncthreads();
+  if (share_bits > 0 && T1 > 0) {
+    // first-block hash in the staging areas (free until the stream starts):
+    // slot = {first block, lowest holder, holders, highest holder}, then a
+    // list of the slots held more than once
+    const int H = 1 << share_bits;
+    int4* slots = reinterpret_cast<int4*>(reinterpret_cast<char*>(s_pre) +
+                                          ((static_cast<int>(sizeof(int)) * (S + 1) + 15) & ~15));
+    int* groups = reinterpret_cast<int*>(slots + H);   // [n_groups]
+    for (int i = tid; i < H; i += kSplitThreads) slots[i] = make_int4(-1, 0x7fffffff, 0, -1);
+    if (tid == 0) s_max[0] = 0;                        // group count
+    __syncthreads();
+    for (int i = 0; i < per; ++i) {
+      const int s = s_lo + i;
+      if (s >= S) break;
+      if (seq_ctx(s) <= 0) continue;
+      const int32_t b0 = read_only(a.block_table + static_cast<int64_t>(s) * a.max_blocks);
+      if (b0 < 0 || b0 >= a.num_blocks) continue;
+      int h = static_cast<int>(share_hash(b0, share_bits));
+      while (true) {
+        const int old = atomicCAS(&slots[h].x, -1, b0);
+        if (old == -1 || old == b0) break;
+        h = (h + 1) & (H - 1);
+      }
+      atomicMin(&slots[h].y, s);
+      atomicMax(&slots[h].w, s);
+      atomicAdd(&slots[h].z, 1);
+    }
+    __syncthreads();
+    for (int h = tid; h < H; h += kSplitThreads)
+      if (slots[h].z > 1) groups[atomicAdd(&s_max[0], 1)] = h;
+    __syncthreads();
+    const int n_groups = s_max[0];
+    const int n_wg = gridDim.x;
+    if (n_groups > 0 && n_wg % kXcds == 0) {
+      // a group's run: the leading blocks its lowest and highest holders
+      // have in common, within both contexts; one wave per group, 64 blocks
+      // compared at a time (into .x)
+      for (int g = w; g < n_groups; g += kSplitThreads / 64) {
+        const int h = groups[g];
+        const int r0 = slots[h].y, r1 = slots[h].w;
+        const int n0 = (seq_ctx(r0) + a.block_size - 1) / a.block_size;
+        const int n1 = (seq_ctx(r1) + a.block_size - 1) / a.block_size;
+        const int lim = n0 < n1 ? n0 : n1;
+        const int32_t* row0 = a.block_table + static_cast<int64_t>(r0) * a.max_blocks;
+        const int32_t* row1 = a.block_table + static_cast<int64_t>(r1) * a.max_blocks;
+        int run = 0;
+        for (int c0 = 0; c0 < lim; c0 += 64) {
+          const int b = c0 + lane;
+          bool same = false;
+          if (b < lim) {
+            const int32_t x0 = row0[b];
+            same = x0 == row1[b] && x0 >= 0 && x0 < a.num_blocks;
+          }
+          const uint64_t diff = ~__ballot(same);
+          if (diff != 0) {
+            run = c0 + static_cast<int>(__builtin_ctzll(diff));
+            break;
+          }
+          run = c0 + 64;
+        }
+        run = run < lim ? run : lim;
+        if (lane == 0) slots[h].x = run;
+      }
+      __syncthreads();
+      // every line of every run, spread over the workgroups of this XCD
+      // (workgroup i runs on XCD i % 8)
+      const int J = n_wg / kXcds;
+      const int j = blockIdx.x / kXcds;
+      const int lpb = a.block_size * kD * 2 / 128;           // lines per (block, head) slab
+      const int64_t head_stride = static_cast<int64_t>(a.block_size) * kD * 2;
+      const int64_t block_stride = head_stride * a.num_kv_heads;
+      const int per_blk = a.num_kv_heads * 2 * lpb;          // lines per block, K and V
+      uint32_t sink = 0;
+      for (int g = 0; g < n_groups; ++g) {
+        const int h = groups[g];
+        const int run = slots[h].x;
+        const int32_t* row = a.block_table + static_cast<int64_t>(slots[h].y) * a.max_blocks;
+        const int lines = run * per_blk;
+        for (int e = j * kSplitThreads + tid; e < lines; e += J * kSplitThreads) {
+          const int ib = e / per_blk;
+          const int r = e % per_blk;
+          const int kvh = r / (2 * lpb);
+          const int kv = (r / lpb) & 1;
+          const int64_t off = static_cast<int64_t>(row[ib]) * block_stride + kvh * head_stride +
+                              static_cast<int64_t>(r % lpb) * 128;
+          sink += *reinterpret_cast<const volatile uint32_t*>(
+              static_cast<const char*>(kv ? a.v_cache : a.k_cache) + off);
+        }
+      }
+      // keeps the loads (the sum means nothing)
+      if (sink == 0x9e3779b9u) s_wsum[0] = static_cast<int>(sink);
+    }
+    __syncthreads();
+  }
   if (T1 == 0) return;
 
   // 2. this wave's KV head and range of the stream. Workgroups are dealt to
@@ -933,16 +1042,25 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
   const bool one = kVar || G >= 4;
   const int per_cu = one ? 1 : sh.per_cu2;
   const size_t dyn = one ? sh.dyn1 : sh.dyn2;
-  // staging area per wave: what the prefix leaves, in whole 16-byte units
+  // staging area per wave: what the prefix leaves, in whole 16-byte units.
+  // Decode calls look for shared blocks when the first-block hash (at least
+  // twice as many slots as sequences) and the sequences' slots fit there.
   const size_t pre = (static_cast<size_t>(a.num_seqs + 1) * sizeof(int) + 15) & ~size_t(15);
   const int stage = static_cast<int>(((dyn - pre) / waves_per_wg) & ~size_t(15));
+  int share_bits = 0;
+  if (!kVar && a.num_seqs > 1) {
+    int bits = 1;
+    while ((1 << bits) < 2 * a.num_seqs) ++bits;
+    if ((static_cast<size_t>(kShareSlotBytes) << bits) + (sizeof(int) << bits) <= dyn - pre)
+      share_bits = bits;
+  }
   // whole groups of num_kv_heads waves, no more than the GPU holds at once
   int64_t waves = static_cast<int64_t>(sh.cus) * per_cu * waves_per_wg;
   int64_t per_kv = waves / a.num_kv_heads;
   if (per_kv < 1) per_kv = 1;
   const int64_t wgs = (per_kv * a.num_kv_heads + waves_per_wg - 1) / waves_per_wg;
   kernel<<<dim3(static_cast<unsigned>(wgs)), dim3(kSplitThreads), dyn, stream>>>(
-      a, static_cast<int>(per_kv), stage);
+      a, static_cast<int>(per_kv), stage, share_bits);
   return hipGetLastError();
 }
 

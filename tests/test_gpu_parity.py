@@ -546,3 +546,61 @@ def test_merged_edge_lengths(dev, pkv):
         kv1 = th["v_cache"][int(b.block_table[1, 0]), :, 0]
         assert torch.equal(got[1].cpu(), kv1.float().repeat_interleave(4, 0))
         assert int(counters.abs().sum()) == 0
+
+
+def test_shared_prefix_groups(dev, pkv):
+    """Several groups of sequences sharing leading blocks (runs of 1 to 6
+    blocks, a group whose members diverge after the first block, a member
+    shorter than the run, single sequences): the split kernel finds them by
+    their first block and reads the shared lines ahead; the output equals
+    the oracle's, split and unsplit, merged in one launch or two."""
+    rng = np.random.default_rng(77)
+    B, N = 16, 400
+    free = [int(x) for x in rng.permutation(N)]
+    rows, lens = [], []
+
+    def take(n):
+        out = free[:n]
+        del free[:n]
+        return out
+
+    for run, members in ((6, 5), (1, 3), (3, 4), (2, 2)):
+        shared = take(run)
+        for m in range(members):
+            L = int(rng.integers(1, 12 * B))
+            if m == 0:
+                L = max(L, run * B)          # the lowest holder covers the run
+            nb = -(-L // B)
+            rows.append((shared + take(max(0, nb - run)))[:nb])
+            lens.append(L)
+    for _ in range(6):
+        L = int(rng.integers(1, 20 * B))
+        rows.append(take(-(-L // B)))
+        lens.append(L)
+    order = rng.permutation(len(rows))
+    rows = [rows[i] for i in order]
+    lens = [lens[i] for i in order]
+    width = max(len(r) for r in rows)
+    table = np.full((len(rows), width), -1, np.int32)
+    for s, r in enumerate(rows):
+        table[s, :len(r)] = r
+    b = W.Batch(name="shared_groups", dtype="bf16", num_heads=32, num_kv_heads=8,
+                head_size=128, block_size=B, num_blocks=N, block_table=table,
+                context_lens=np.array(lens, np.int32), free_order=np.arange(N, dtype=np.int32),
+                seed=4244)
+    say(f"case: shared prefix groups S={b.num_seqs}")
+    t = W.layer_tensors(b, device=dev)
+    th = host(t)
+    want = oracle_attention(b, th["q"], th["k_cache"], th["v_cache"])
+    meta = device_meta(b, dev)
+    counters = torch.zeros(b.num_seqs * b.num_kv_heads, dtype=torch.int32, device=dev)
+    for P in (0, 16, 64):
+        got = gpu_attention(pkv, b, t, meta, dev, P)
+        torch.cuda.synchronize()
+        e = max_err(got.cpu(), want)
+        say(f"  P={P}: max abs err {e:.3e}")
+        assert e <= TOL
+        if P:
+            m = _merged(pkv, b, t, meta, dev, P, b.max_partitions(P), counters)
+            torch.cuda.synchronize()
+            assert max_err(m.cpu(), want) <= TOL
