@@ -1,12 +1,14 @@
 """Benchmark of the paged-KV decode hot path on one MI355X.
 
 Default workload: the full decode step -- 512 sequences, cached lengths
-U{64..4096}, 32 layers, bf16, Hq=32, Hkv=8, D=128, block 16. One step = one
-slot-mapping launch for the batch, then for every layer: the new tokens' K/V
-write, and split decode attention (balanced pieces, 1024-position slots) with
-its log-sum-exp merge in the same launch (paged_decode_attention_merged;
-``--merge two-launch`` runs the split call and paged_attention_reduce
-instead, as the single-layer workloads do by default).
+U{64..4096}, 32 layers, bf16, Hq=32, Hkv=8, D=128, block 16. One step = for
+every layer one paged_decode_attention_append launch: each sequence's new
+token K/V stored at the slot its position translates to (slot mapping and
+write), split decode attention (balanced pieces, 1024-position slots) and the
+log-sum-exp merge. ``--write separate`` runs paged_slot_mapping once and
+paged_kv_write per layer before a paged_decode_attention_merged launch;
+``--merge two-launch`` the split call and paged_attention_reduce (as the
+single-layer workloads do by default).
 Inputs are resident in HBM before timing starts.
 
 Multi-token workloads (``--workload spec_verify_bf16`` / ``mixed_prefill_bf16``):
@@ -535,6 +537,10 @@ def main():
                          "its sequences finish in one piece), two for the single-layer cases "
                          "(many pieces per sequence: the in-kernel merge lengthens the kernel's "
                          "tail by about what the second launch costs)")
+    ap.add_argument("--write", choices=["fused", "separate"], default="fused",
+                    help="decode step with the merge in one launch: store the new tokens' K/V in "
+                         "the same launch (paged_decode_attention_append) or with "
+                         "paged_slot_mapping + paged_kv_write first")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured in a HIP graph (per-kernel times "
                          "still come from eager steps)")
@@ -628,10 +634,19 @@ def main():
         e1.record()
         ev[name].append((e0, e1))
 
+    fused_write = pos is not None and P > 0 and not args.two_call and args.write == "fused"
+
     def step(record=()):
-        if pos is not None:
+        if pos is not None and not fused_write:
             pkv.paged_slot_mapping(slots, table, pos, batch.block_size)
         for l, t in enumerate(layers):
+            if fused_write:
+                # the new token's K/V stored at its slot, attention and merge:
+                # one launch per layer
+                timed("decode", record, lambda: pkv.paged_decode_attention_append(
+                    outs[l], t["q"], t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], table,
+                    ctx, scale, P, mp, ml, es, to, counters))
+                continue
             if pos is not None:
                 timed("write", record, lambda: pkv.paged_kv_write(
                     t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], slots))
@@ -802,9 +817,11 @@ def main():
                      "traffic": traffic,
                      "kernel": "paged_varlen_attention (split kernel, prefill kernel, merge)"
                      if varlen
-                     else "decode_split_kernel" + ("" if args.two_call else
-                                                   " (paged_decode_attention_merged: pieces "
-                                                   "merged in the same launch)")
+                     else "decode_split_kernel" + (
+                         "" if args.two_call else
+                         " (paged_decode_attention_append: new tokens' K/V stored, pieces merged, "
+                         "in the same launch)" if fused_write else
+                         " (paged_decode_attention_merged: pieces merged in the same launch)")
                      if P > 0 else "decode_whole_kernel",
                      "bytes_per_launch": layer_bytes,
                      "logical_bytes_per_launch": logical_bytes,

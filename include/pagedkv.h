@@ -202,6 +202,37 @@ int paged_decode_attention_merged(float* out, const void* query, const void* k_c
                                   void* stream);
 
 /*
+ * paged_decode_attention_append -- one decode step of one layer: each
+ * sequence's new token K/V written into the paged pools, then
+ * paged_decode_attention_merged over the updated pools.
+ *
+ * Sequence s's new token is its last position p = ctx_s - 1 (context_lens
+ * count it). Its rows k_new[s], v_new[s] ([num_seqs, num_kv_heads,
+ * head_size] dtype) are stored at the slot p translates to,
+ * block_table[s][p / B] * B + p % B -- what paged_slot_mapping at positions
+ * ctx - 1 followed by paged_kv_write stores (the backend writes the new
+ * token's K/V to its slot: "vLLM PagedAttention ...", section 6) -- and out
+ * is the attention over positions 0 .. ctx_s - 1 including it. On the fast
+ * path this is one launch: the wave that reads the tile holding p stores the
+ * new rows for its KV head before it loads that tile; elsewhere it is the
+ * write, the plain split kernel and the merge. Arguments and workspace as
+ * paged_decode_attention_merged, plus the mutable pools and k_new / v_new
+ * (device). Preconditions: as paged_kv_write (each sequence owns the block
+ * its new token goes to; a shared block is copied first, copy-on-write).
+ * Sequences with ctx_s == 0 write nothing and get out = 0.
+ * Errors: those of paged_decode_attention_merged, PKV_ERR_NULL for NULL
+ * k_new / v_new.
+ */
+int paged_decode_attention_append(float* out, const void* query, void* k_cache, void* v_cache,
+                                  const void* k_new, const void* v_new,
+                                  const int32_t* block_table, const int32_t* context_lens,
+                                  int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                                  int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                                  float scale, int partition_size, int max_partitions,
+                                  float* max_logits, float* exp_sums, float* tmp_out,
+                                  int32_t* counters, int dtype, void* stream);
+
+/*
  * paged_attention_reduce -- merge split partials into the final output.
  *
  * For each (s, h) with ctx_s >= 1, over the slots p < max_partitions with

@@ -29,6 +29,9 @@ SIGNATURES = {
     "paged_decode_attention_merged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                              _I32, _I64, _I32, _F32, _I32, _I32, _P, _P, _P, _P,
                                              _I32, _P]),
+    "paged_decode_attention_append": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                             _I32, _I32, _I64, _I32, _F32, _I32, _I32, _P, _P,
+                                             _P, _P, _I32, _P]),
     "paged_attention_reduce": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
     "paged_varlen_attention": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                       _I32, _I32, _I64, _I32, _F32, _I32, _P, _P, _P, _I32,
@@ -215,6 +218,38 @@ def paged_decode_attention_merged(out, query, k_cache, v_cache, block_table, con
         _ptr(context_lens), s, hq, hkv, d, b, n, block_table.shape[1], float(scale),
         partition_size, max_partitions, _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out),
         _ptr(counters), _DTYPE[query.dtype], _stream(stream)))
+
+
+def paged_decode_attention_append(out, query, k_cache, v_cache, k_new, v_new, block_table,
+                                  context_lens, scale, partition_size, max_partitions, max_logits,
+                                  exp_sums, tmp_out, counters, stream=None):
+    """One decode step of one layer: each sequence's new token k_new / v_new
+    [S, Hkv, D] stored at its last position (context_lens - 1), then split
+    attention merged into out [S, Hq, D]; counters [S * Hkv] int32 are zero
+    before and after the call."""
+    n, hkv, b, d = _pool_geometry(k_cache, v_cache)
+    _need(query.dim() == 3 and query.shape[2] == d, "query is [num_seqs, Hq, D]")
+    _need(query.dtype == k_cache.dtype, "query and pools differ in dtype")
+    s, hq, _ = query.shape
+    _need(k_new.shape == (s, hkv, d) and v_new.shape == k_new.shape,
+          "k_new / v_new are [num_seqs, Hkv, D]")
+    _need(k_new.dtype == v_new.dtype == k_cache.dtype, "new K/V and pools differ in dtype")
+    _i32(block_table, context_lens, counters)
+    _need(block_table.dim() == 2 and block_table.shape[0] == s,
+          "block_table is [num_seqs, max_blocks]")
+    _need(context_lens.numel() == s, "context_lens has one entry per sequence")
+    _need(partition_size > 0, "the call splits: partition_size > 0")
+    _workspace(s * hq, max_partitions, d, max_logits, exp_sums, tmp_out)
+    _need(out is not None and out.dtype == torch.float32 and out.numel() == s * hq * d,
+          "out is float32 [num_seqs, Hq, D]")
+    _need(counters.numel() >= s * hkv, "counters need num_seqs x Hkv entries")
+    _dev(out, query, k_cache, v_cache, k_new, v_new, block_table, context_lens, max_logits,
+         exp_sums, tmp_out, counters)
+    _check("paged_decode_attention_append", lib.paged_decode_attention_append(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+        _ptr(block_table), _ptr(context_lens), s, hq, hkv, d, b, n, block_table.shape[1],
+        float(scale), partition_size, max_partitions, _ptr(max_logits), _ptr(exp_sums),
+        _ptr(tmp_out), _ptr(counters), _DTYPE[query.dtype], _stream(stream)))
 
 
 def paged_attention_reduce(out, max_logits, exp_sums, tmp_out, context_lens, partition_size,

@@ -262,6 +262,49 @@ int paged_decode_attention_merged(float* out, const void* query, const void* k_c
                                           max_partitions, as_stream(stream)));
 }
 
+int paged_decode_attention_append(float* out, const void* query, void* k_cache, void* v_cache,
+                                  const void* k_new, const void* v_new,
+                                  const int32_t* block_table, const int32_t* context_lens,
+                                  int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                                  int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                                  float scale, int partition_size, int max_partitions,
+                                  float* max_logits, float* exp_sums, float* tmp_out,
+                                  int32_t* counters, int dtype, void* stream) {
+  if (partition_size < 1) return PKV_ERR_SHAPE;
+  pkv::DecodeArgs a{};
+  const int rc = decode_args(a, out, query, k_cache, v_cache, block_table, context_lens,
+                             num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                             num_blocks, max_blocks_per_seq, scale, partition_size,
+                             max_partitions, max_logits, exp_sums, tmp_out, dtype);
+  if (rc != kLaunch) return rc;
+  if (!out || !k_new || !v_new) return PKV_ERR_NULL;
+  if (!counters) return PKV_ERR_WORKSPACE;
+  // the write's grid is one thread per 2-byte chunk at worst
+  const int64_t chunks = static_cast<int64_t>(num_seqs) * num_kv_heads *
+                         (static_cast<int64_t>(head_size) * elem_bytes(dtype) / 2);
+  if (chunks / 256 >= 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  if (pkv::fast_decode_supported(a)) {
+    a.counters = counters;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    return launch_status(pkv::launch_decode_fast(a, as_stream(stream)));
+  }
+  // elsewhere: the write (each sequence's last position), the plain split
+  // kernel, the merge
+  if (num_seqs > kMaxGridYZ || num_heads > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  hipError_t e = pkv::launch_kv_write(k_cache, v_cache, k_new, v_new, nullptr, num_seqs,
+                                      num_blocks, num_kv_heads, block_size, head_size,
+                                      elem_bytes(dtype), as_stream(stream), block_table,
+                                      context_lens, max_blocks_per_seq);
+  if (e != hipSuccess) return PKV_ERR_LAUNCH;
+  a.out = nullptr;
+  e = pkv::launch_decode_generic(a, as_stream(stream));
+  if (e != hipSuccess) return PKV_ERR_LAUNCH;
+  return launch_status(pkv::launch_reduce(out, max_logits, exp_sums, tmp_out, context_lens,
+                                          num_seqs, num_heads, head_size, partition_size,
+                                          max_partitions, as_stream(stream)));
+}
+
 int paged_attention_reduce(float* out, const float* max_logits, const float* exp_sums,
                            const float* tmp_out, const int32_t* context_lens, int num_seqs,
                            int num_heads, int head_size, int partition_size, int max_partitions,

@@ -47,12 +47,16 @@ template <> struct Chunk<2> { using type = uint16_t; };
 // One thread per W-byte chunk of one (token, kv head) row, for K and V.
 // The backend writes new K/V to the slots the slot mapping names ("vLLM
 // PagedAttention ...", section 6); slot s is block s / B, offset s % B.
+// Without a slot mapping (slot_mapping == NULL) token i is the last
+// position ctx_i - 1 of sequence i, stored where that position translates
+// through the sequence's table row.
 template <int W>
 __global__ void kv_write_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
                                 const char* __restrict__ k_new, const char* __restrict__ v_new,
                                 const int64_t* __restrict__ slot_mapping, int64_t num_tokens,
                                 int64_t num_slots, int num_kv_heads, int block_size,
-                                int row_bytes) {
+                                int row_bytes, const int32_t* __restrict__ block_table,
+                                const int32_t* __restrict__ context_lens, int max_blocks) {
   using T = typename Chunk<W>::type;
   const int cpr = row_bytes / W;  // chunks per (token, head) row
   int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -62,7 +66,15 @@ __global__ void kv_write_kernel(char* __restrict__ k_cache, char* __restrict__ v
   int64_t r = g / cpr;
   int h = static_cast<int>(r % num_kv_heads);
   int64_t i = r / num_kv_heads;
-  int64_t slot = slot_mapping[i];
+  int64_t slot = -1;
+  if (slot_mapping != nullptr) {
+    slot = slot_mapping[i];
+  } else {
+    const int p = context_lens[i] - 1;
+    const int64_t b = physical_block(block_table + i * max_blocks, p, block_size, max_blocks,
+                                     num_slots / block_size);
+    slot = b >= 0 ? b * block_size + p % block_size : -1;
+  }
   if (slot < 0 || slot >= num_slots) return;
   int64_t blk = slot / block_size;
   int off = static_cast<int>(slot % block_size);
@@ -84,7 +96,8 @@ static int chunk_width(int row_bytes, const void* const* ptrs, int n) {
 hipError_t launch_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                            const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
                            int num_kv_heads, int block_size, int head_size, int elem_bytes,
-                           hipStream_t stream) {
+                           hipStream_t stream, const int32_t* block_table,
+                           const int32_t* context_lens, int max_blocks) {
   int row_bytes = head_size * elem_bytes;
   const void* ptrs[4] = {k_cache, v_cache, k_new, v_new};
   int w = chunk_width(row_bytes, ptrs, 4);
@@ -100,22 +113,26 @@ hipError_t launch_kv_write(void* k_cache, void* v_cache, const void* k_new, cons
     case 16:
       kv_write_kernel<16><<<blocks, threads, 0, stream>>>(kc, vc, kn, vn, slot_mapping,
                                                           num_tokens, num_slots, num_kv_heads,
-                                                          block_size, row_bytes);
+                                                          block_size, row_bytes, block_table,
+                                                          context_lens, max_blocks);
       break;
     case 8:
       kv_write_kernel<8><<<blocks, threads, 0, stream>>>(kc, vc, kn, vn, slot_mapping,
                                                          num_tokens, num_slots, num_kv_heads,
-                                                         block_size, row_bytes);
+                                                         block_size, row_bytes, block_table,
+                                                         context_lens, max_blocks);
       break;
     case 4:
       kv_write_kernel<4><<<blocks, threads, 0, stream>>>(kc, vc, kn, vn, slot_mapping,
                                                          num_tokens, num_slots, num_kv_heads,
-                                                         block_size, row_bytes);
+                                                         block_size, row_bytes, block_table,
+                                                         context_lens, max_blocks);
       break;
     default:
       kv_write_kernel<2><<<blocks, threads, 0, stream>>>(kc, vc, kn, vn, slot_mapping,
                                                          num_tokens, num_slots, num_kv_heads,
-                                                         block_size, row_bytes);
+                                                         block_size, row_bytes, block_table,
+                                                         context_lens, max_blocks);
   }
   return hipGetLastError();
 }

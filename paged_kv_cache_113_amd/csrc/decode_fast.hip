@@ -513,6 +513,10 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     T1 += s_wsum[i];
     n_max = s_max[i] > n_max ? s_max[i] : n_max;
   }
+  // (shared-block detection, below: each sequence's first block, kept in the
+  // staging areas, which are free until the stream starts)
+  int* first_of = reinterpret_cast<int*>(reinterpret_cast<char*>(s_pre) +
+                                         ((static_cast<int>(sizeof(int)) * (S + 1) + 15) & ~15));
   {
     int run = base + incl - local;  // exclusive prefix of this thread's chunk
     for (int i = 0; i < per; ++i) {
@@ -521,6 +525,8 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
         s_pre[s] = run;
         int last;
         run += seq_tiles(s, last);
+        if (share_bits > 0)
+          first_of[s] = read_only(a.block_table + static_cast<int64_t>(s) * a.max_blocks);
       }
     }
     if (tid == 0) s_pre[S] = T1;
@@ -541,8 +547,8 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     // slot = {first block, lowest holder, holders, highest holder}, then a
     // list of the slots held more than once
     const int H = 1 << share_bits;
-    int4* slots = reinterpret_cast<int4*>(reinterpret_cast<char*>(s_pre) +
-                                          ((static_cast<int>(sizeof(int)) * (S + 1) + 15) & ~15));
+    int4* slots = reinterpret_cast<int4*>(reinterpret_cast<char*>(first_of) +
+                                          ((static_cast<int>(sizeof(int)) * S + 15) & ~15));
     int* groups = reinterpret_cast<int*>(slots + H);   // [n_groups]
     for (int i = tid; i < H; i += kSplitThreads) slots[i] = make_int4(-1, 0x7fffffff, 0, -1);
     if (tid == 0) s_max[0] = 0;                        // group count
@@ -550,8 +556,8 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     for (int i = 0; i < per; ++i) {
       const int s = s_lo + i;
       if (s >= S) break;
-      if (seq_ctx(s) <= 0) continue;
-      const int32_t b0 = read_only(a.block_table + static_cast<int64_t>(s) * a.max_blocks);
+      if (s_pre[s + 1] == s_pre[s]) continue;          // no positions
+      const int32_t b0 = first_of[s];
       if (b0 < 0 || b0 >= a.num_blocks) continue;
       int h = static_cast<int>(share_hash(b0, share_bits));
       while (true) {
@@ -922,7 +928,41 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   // tile also covers it. Each processed tile has exactly one tile of loads
   // behind it, or none, on every path.
   TileRegs ta, tb;
+  // Decode step: the new token of each sequence whose last tile lies in this
+  // range goes into the pool here, for this wave's KV head, by the wave that
+  // reads that tile (the only reader of that row in this launch): its later
+  // load of the tile comes after the store from the same wave, so it sees
+  // the new row. Lanes 0-15 store the K row's 16-byte chunks, lanes 16-31 the
+  // V row's, for up to two sequences per round (lanes 32-63).
+  auto append_new_tokens = [&]() {
+    const int b1 = b0 + len;
+    const int half = lane >> 5;
+    const int which = (lane >> 4) & 1;
+    const int chunk = lane & 15;
+    const char* src_base = static_cast<const char*>(which ? a.v_new : a.k_new);
+    char* dst_base = const_cast<char*>(which ? geo.vc : geo.kc);
+    for (int s0 = lo; s0 < S && pre(s0) < b1; s0 += 2) {
+      const int s = s0 + half;
+      if (s < S && s_pre[s + 1] > s_pre[s] && s_pre[s + 1] - 1 >= b0 && s_pre[s + 1] - 1 < b1) {
+        const int p = seq_ctx(s) - 1;
+        const int64_t blk = physical_block(row_of(s), p, a.block_size, a.max_blocks,
+                                           a.num_blocks);
+        const uint4 x = *reinterpret_cast<const uint4*>(
+            src_base + ((static_cast<int64_t>(s) * a.num_kv_heads + kvh) * kD) * 2 + chunk * 16);
+        if (blk >= 0)
+          store_untracked(dst_base + blk * geo.block_stride + kvh * geo.head_stride +
+                              static_cast<int64_t>(p % a.block_size) * kD * 2 + chunk * 16,
+                          x);
+      }
+    }
+  };
+  // when this range starts with such a tile, the store must come first;
+  // otherwise the first tile's loads go out first
+  const bool append = !kVar && a.k_new != nullptr;
+  const bool first_is_new = append && pre(cur.s + 1) - 1 == b0;
+  if (first_is_new) append_new_tokens();
   bool ga = geo.load(ta, row_of(cur.s), cur.t * kTile, kvh);
+  if (append && !first_is_new) append_new_tokens();
   bool gb = true;
   Cursor nx = cur;
   int i = 0;
@@ -1051,7 +1091,9 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
   if (!kVar && a.num_seqs > 1) {
     int bits = 1;
     while ((1 << bits) < 2 * a.num_seqs) ++bits;
-    if ((static_cast<size_t>(kShareSlotBytes) << bits) + (sizeof(int) << bits) <= dyn - pre)
+    const size_t first = (sizeof(int) * static_cast<size_t>(a.num_seqs) + 15) & ~size_t(15);
+    if (first + (static_cast<size_t>(kShareSlotBytes) << bits) + (sizeof(int) << bits) <=
+        dyn - pre)
       share_bits = bits;
   }
   // whole groups of num_kv_heads waves, no more than the GPU holds at once

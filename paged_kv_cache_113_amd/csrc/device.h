@@ -81,6 +81,12 @@ __device__ __forceinline__ void store_untracked(float* p, float4 v) {
 __device__ __forceinline__ void store_untracked(float* p, float v) {
   asm volatile("global_store_dword %0, %1, off\n\ts_nop 1" : : "v"(p), "v"(v));
 }
+// A 16-byte store of raw data, untracked like the stores above.
+__device__ __forceinline__ void store_untracked(void* p, uint4 v) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t x = {v.x, v.y, v.z, v.w};
+  asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" : : "v"(p), "v"(x));
+}
 // The same stores at device scope (sc1): written through to the memory side,
 // where waves of the other XCDs read them with device-scope loads, once the
 // issuing wave has waited for them (s_waitcnt vmcnt(0)).

@@ -12,10 +12,13 @@ hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table
                                const int32_t* positions, int num_seqs, int max_blocks,
                                int block_size, hipStream_t stream);
 
+// slot_mapping NULL: token i is sequence i's last position (ctx_i - 1),
+// stored where that position translates through block_table.
 hipError_t launch_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                            const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
                            int num_kv_heads, int block_size, int head_size, int elem_bytes,
-                           hipStream_t stream);
+                           hipStream_t stream, const int32_t* block_table = nullptr,
+                           const int32_t* context_lens = nullptr, int max_blocks = 0);
 
 hipError_t launch_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                             const int32_t* block_table, const int32_t* context_lens,
@@ -46,6 +49,11 @@ struct DecodeArgs {
   // split decode merged in the same launch: [num_seqs * num_kv_heads]
   // arrival counters, zero on entry and left zero; NULL otherwise
   int32_t* counters;
+  // decode step: the new tokens' K/V [num_seqs, Hkv, D]; the split kernel
+  // stores each at its sequence's last position before reading it; NULL
+  // otherwise
+  const void* k_new;
+  const void* v_new;
 };
 
 // Matrix-core path: f16/bf16, head_size 128, block_size % 16 == 0, G <= 16.

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
               "paged_slot_mapping", "paged_kv_gather", "paged_attention_workspace_bytes",
               "paged_varlen_attention", "paged_kv_copy_blocks", "paged_kv_swap_out",
               "paged_kv_swap_in", "paged_varlen_attention_noalloc",
-              "paged_decode_attention_merged", "pkv_strerror"):
+              "paged_decode_attention_merged", "paged_decode_attention_append",
+              "pkv_strerror"):
         assert n in names
 
 
@@ -177,6 +178,27 @@ def test_merged_validation(lib):
     assert merged(ctr=None) == EWS
     assert merged(to=None) == EWS
     assert merged(q=None) == ENULL
+
+
+def test_append_validation(lib):
+    """The append call checks what the merged call checks, plus the new
+    tokens' K/V, before any HIP call."""
+    def append(**kw):
+        a = dict(out=P, q=P, k=P, v=P, kn=P, vn=P, table=P, ctx=P, S=2, Hq=8, Hkv=2, D=128,
+                 B=16, N=10, MB=4, scale=0.1, P=16, mp=4, ml=P, es=P, to=P, ctr=P, dtype=2)
+        a.update(kw)
+        return lib.paged_decode_attention_append(
+            a["out"], a["q"], a["k"], a["v"], a["kn"], a["vn"], a["table"], a["ctx"], a["S"],
+            a["Hq"], a["Hkv"], a["D"], a["B"], a["N"], a["MB"], a["scale"], a["P"], a["mp"],
+            a["ml"], a["es"], a["to"], a["ctr"], a["dtype"], None)
+    assert append(P=0) == ESHAPE
+    assert append(dtype=7) == EDTYPE
+    assert append(S=0) == OK
+    assert append(kn=None) == ENULL
+    assert append(vn=None) == ENULL
+    assert append(out=None) == ENULL
+    assert append(ctr=None) == EWS
+    assert append(k=None) == ENULL
 
 
 EHOST = -7

@@ -604,3 +604,77 @@ def test_shared_prefix_groups(dev, pkv):
             m = _merged(pkv, b, t, meta, dev, P, b.max_partitions(P), counters)
             torch.cuda.synchronize()
             assert max_err(m.cpu(), want) <= TOL
+
+
+# -- one decode step of one layer in one call ---------------------------------------
+
+APPEND = {
+    "decode_step_small": lambda: W.decode_step_bf16(num_seqs=32, lo=1, hi=200, num_layers=1),
+    "decode_step_short": lambda: W.decode_step_bf16(num_seqs=300, lo=1, hi=40, num_layers=1),
+    "gqa8_f16_step": lambda: W._uniform_case("gqa8_step", "f16", 64, 8, 128, 32, 7, 1, 700, 83,
+                                             new_token=True),
+    "plain_f32_step": lambda: W._uniform_case("plain_step", "f32", 8, 2, 64, 8, 5, 1, 100, 84,
+                                              new_token=True),
+}
+
+
+def _append(pkv, b, t, meta, dev, P, mp, counters):
+    out = torch.full((b.num_seqs, b.num_heads, b.head_size), float("nan"), device=dev)
+    shape = (b.num_seqs, b.num_heads, mp)
+    ml = torch.full(shape, float("nan"), device=dev)
+    es = torch.full(shape, float("nan"), device=dev)
+    to = torch.full(shape + (b.head_size,), float("nan"), device=dev)
+    pkv.paged_decode_attention_append(out, t["q"], t["k_cache"], t["v_cache"], t["k_new"],
+                                      t["v_new"], meta["table"], meta["ctx"], scale_of(b), P, mp,
+                                      ml, es, to, counters)
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(APPEND))
+def test_append_call(dev, pkv, name):
+    """paged_decode_attention_append: the pools afterwards are bit for bit the
+    oracle's scatter of the new tokens at the oracle's slots (positions
+    ctx - 1), and the output is within 2e-3 of the oracle's attention over
+    them; twice in a row on the same counters (left at zero), bit-equal."""
+    b = APPEND[name]()
+    P = 4 * b.block_size
+    mp = b.max_partitions(P)
+    say(f"case: append {name} S={b.num_seqs} P={P} mp={mp}")
+    t = W.layer_tensors(b, device=dev)
+    th = host(t)
+    k, v, _ = oracle_pools_after_write(b, th)
+    meta = device_meta(b, dev)
+    counters = torch.zeros(b.num_seqs * b.num_kv_heads, dtype=torch.int32, device=dev)
+    first = _append(pkv, b, t, meta, dev, P, mp, counters)
+    second = _append(pkv, b, t, meta, dev, P, mp, counters)
+    torch.cuda.synchronize()
+    bits = lambda x: np.ascontiguousarray(x).view(np.uint8)   # noqa: E731  (NaN poison)
+    assert np.array_equal(bits(oracle._raw(t["k_cache"].cpu(), b.dtype)), bits(k))
+    assert np.array_equal(bits(oracle._raw(t["v_cache"].cpu(), b.dtype)), bits(v))
+    assert int(counters.abs().sum()) == 0
+    assert torch.equal(first, second)
+    e = max_err(first.cpu(), oracle_attention(b, th["q"], k, v))
+    say(f"  max abs err {e:.3e}")
+    assert e <= TOL
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_append_decode_step_full_size(dev, pkv, layer):
+    """The benchmark's call on a whole layer of the 32-layer decode step
+    (512 sequences, partition size 1024): pools bit-exact after the write,
+    every sequence's attention against the oracle."""
+    b = W.decode_step_bf16()
+    say(f"case: append full decode step layer {layer}")
+    t = W.layer_tensors(b, layer=layer, device=dev)
+    th = host(t)
+    k, v, _ = oracle_pools_after_write(b, th)
+    meta = device_meta(b, dev)
+    counters = torch.zeros(b.num_seqs * b.num_kv_heads, dtype=torch.int32, device=dev)
+    out = _append(pkv, b, t, meta, dev, 1024, b.max_partitions(1024), counters)
+    torch.cuda.synchronize()
+    assert np.array_equal(oracle._raw(t["k_cache"].cpu(), b.dtype), k)
+    assert np.array_equal(oracle._raw(t["v_cache"].cpu(), b.dtype), v)
+    assert int(counters.abs().sum()) == 0
+    e = max_err(out.cpu(), oracle_attention(b, th["q"], k, v))
+    say(f"  all {b.num_seqs} seqs: max abs err {e:.3e}")
+    assert e <= TOL
