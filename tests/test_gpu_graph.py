@@ -1,4 +1,5 @@
-"""The decode step under graph capture: slot mapping, the K/V write, split
+"""The decode step under graph capture (both the two-launch path and the one
+launch per layer the benchmark times): slot mapping, the K/V write, split
 attention and the merge of two layers captured once in a torch CUDA graph
 (a HIP graph on ROCm) and replayed several times, with the program's own
 eager work and synchronisations between replays; every replay must equal
@@ -76,6 +77,63 @@ def test_decode_step_graph_replays_equal_eager(dev, pkv):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
+        for l, (o, want) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, want), (r, l)
+        print(f"  replay {r}: equal to eager", flush=True)
+
+
+def test_append_step_graph_replays_equal_eager(dev, pkv):
+    """The benchmark's decode step (one paged_decode_attention_append launch
+    per layer: the new tokens' K/V stored, split attention and the in-kernel
+    merge, whose arrival counters each launch leaves at zero) captured once
+    and replayed four times, with eager work between replays: every replay
+    bit-equal to the eager step, the counters zero after each, and the
+    eager step within 2e-3 of the oracle."""
+    b = W.decode_step_bf16(num_seqs=48, lo=1, hi=900, num_layers=2)
+    print(f"case: graph capture of a 2-layer append step, S={b.num_seqs}", flush=True)
+    layers = [W.layer_tensors(b, layer=l, device=dev) for l in range(b.num_layers)]
+    pre = [host(t) for t in layers]
+    meta = device_meta(b, dev)
+    scale = scale_of(b)
+    P = 256
+    mp = b.max_partitions(P)
+    S, H, D = b.num_seqs, b.num_heads, b.head_size
+    outs = [torch.empty(S, H, D, device=dev) for _ in layers]
+    ml = torch.empty(S, H, mp, device=dev)
+    es = torch.empty_like(ml)
+    to = torch.empty(S, H, mp, D, device=dev)
+    counters = torch.zeros(S * b.num_kv_heads, dtype=torch.int32, device=dev)
+
+    def step():
+        for t, out in zip(layers, outs):
+            pkv.paged_decode_attention_append(out, t["q"], t["k_cache"], t["v_cache"], t["k_new"],
+                                              t["v_new"], meta["table"], meta["ctx"], scale, P,
+                                              mp, ml, es, to, counters)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    for l, (o, th) in enumerate(zip(eager, pre)):
+        k, v, _ = oracle_pools_after_write(b, th)
+        e = max_err(o.cpu(), oracle_attention(b, th["q"], k, v))
+        print(f"  eager layer {l}: max abs err {e:.3e}", flush=True)
+        assert e <= TOL
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        to.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(counters.abs().sum()) == 0, r
         for l, (o, want) in enumerate(zip(outs, eager)):
             assert torch.equal(o, want), (r, l)
         print(f"  replay {r}: equal to eager", flush=True)
