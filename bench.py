@@ -765,10 +765,8 @@ def main():
 
     probe = None
     if not args.no_probe:
-        G = batch.num_heads // batch.num_kv_heads
         tph = max(1, batch.block_size * batch.head_size * 2 // 4096)
-        probe = read_probe(dev, layer_bytes, batch.num_kv_heads, tph,
-                           1 if (varlen or G >= 4) else 2)
+        probe = read_probe(dev, layer_bytes, batch.num_kv_heads, tph, 1)
 
     cpu = None
     if cpu_host is not None:

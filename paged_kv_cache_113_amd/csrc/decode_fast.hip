@@ -1000,38 +1000,32 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     });
 }
 
-// Launch shapes of the split kernel on one device. The kernel is
-// register-bound at two workgroups per CU; it runs either two per CU, each
-// with half the CU's LDS, or one per CU with all of it (a staging area twice
-// as large). Its dynamic LDS holds the tile prefix and the staging areas.
-// Computed on first use and kept: the answers only depend on the device and
-// the kernel, and the queries cost host time that would otherwise sit
-// between back-to-back launches.
+// Launch shape of the split kernel on one device: one workgroup per CU with
+// all of the CU's LDS (the tile prefix, then the staging areas). Computed on
+// first use and kept: the answers only depend on the device and the kernel,
+// and the queries cost host time that would otherwise sit between
+// back-to-back launches.
 constexpr int kMaxDevices = 64;
 
 struct SplitShape {
   int cus;
-  int per_cu2;   // resident workgroups with dyn2 (two, unless the device differs)
-  size_t dyn2;   // dynamic LDS per workgroup, two per CU
-  size_t dyn1;   // dynamic LDS per workgroup, one per CU
+  size_t dyn;  // dynamic LDS per workgroup
 };
 
 template <typename T, bool kVar>
 hipError_t split_shape(SplitShape& out) {
-  static std::atomic<int> cache[kMaxDevices][4];  // cus, per_cu2, dyn2, dyn1; 0 = not yet
+  static std::atomic<int> cache[kMaxDevices][2];  // cus, dyn; 0 = not yet
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const bool cached = dev >= 0 && dev < kMaxDevices;
   if (cached) {
     out.cus = cache[dev][0].load(std::memory_order_relaxed);
-    out.per_cu2 = cache[dev][1].load(std::memory_order_relaxed);
-    out.dyn2 = static_cast<size_t>(cache[dev][2].load(std::memory_order_relaxed));
-    out.dyn1 = static_cast<size_t>(cache[dev][3].load(std::memory_order_relaxed));
-    if (out.cus > 0 && out.per_cu2 > 0 && out.dyn2 > 0 && out.dyn1 > 0) return hipSuccess;
+    out.dyn = static_cast<size_t>(cache[dev][1].load(std::memory_order_relaxed));
+    if (out.cus > 0 && out.dyn > 0) return hipSuccess;
   }
   auto kernel = decode_split_kernel<T, kVar>;
-  int cus = 0, lds_cu = 0, per_cu2 = 0;
+  int cus = 0, lds_cu = 0;
   hipFuncAttributes fa;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
@@ -1040,23 +1034,15 @@ hipError_t split_shape(SplitShape& out) {
   if (e != hipSuccess) return e;
   // the prefix alone must always fit
   const size_t need = ((static_cast<size_t>(kMaxSeqsBalanced) + 1) * sizeof(int) + 15) & ~size_t(15);
-  auto budget = [&](int per_cu) {
-    size_t d = static_cast<size_t>(lds_cu) / per_cu;
-    d = d > fa.sharedSizeBytes + 1024 ? (d - fa.sharedSizeBytes - 1024) & ~size_t(1023) : 0;
-    return d < need ? need : d;
-  };
-  const size_t dyn2 = budget(2), dyn1 = budget(1);
+  size_t dyn = static_cast<size_t>(lds_cu);
+  dyn = dyn > fa.sharedSizeBytes + 1024 ? (dyn - fa.sharedSizeBytes - 1024) & ~size_t(1023) : 0;
+  dyn = dyn < need ? need : dyn;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dyn1));
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu2, kernel, kSplitThreads, dyn2);
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dyn));
   if (e != hipSuccess) return e;
-  if (per_cu2 < 1) per_cu2 = 1;
-  out = SplitShape{cus, per_cu2, dyn2, dyn1};
+  out = SplitShape{cus, dyn};
   if (cached) {
-    cache[dev][3].store(static_cast<int>(dyn1), std::memory_order_relaxed);
-    cache[dev][2].store(static_cast<int>(dyn2), std::memory_order_relaxed);
-    cache[dev][1].store(per_cu2, std::memory_order_relaxed);
+    cache[dev][1].store(static_cast<int>(dyn), std::memory_order_relaxed);
     cache[dev][0].store(cus, std::memory_order_relaxed);
   }
   return hipSuccess;
@@ -1069,19 +1055,16 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = split_shape<T, kVar>(sh);
   if (e != hipSuccess) return e;
   const int waves_per_wg = kSplitThreads / 64;
-  // One workgroup per CU, with all of its LDS, for multi-token queries and
-  // for decode with 4+ query heads per KV head: each tile then carries
-  // enough matrix work for one wave per SIMD to keep its loads flowing;
-  // ranges twice as long halve the pieces, and a staging area twice as large
-  // holds more of them until the range ends (multi-token pieces fill all 16
-  // columns: 8.3 KiB each). Measured on MI355X against two per CU: long
-  // split +3.9 %, GQA with a shared prefix +1.5 %, speculative verify +7.7 %,
-  // mixed step +2.5 %, decode step level; MHA (one query head per KV head)
-  // is faster with two.
-  const int G = a.num_heads / a.num_kv_heads;
-  const bool one = kVar || G >= 4;
-  const int per_cu = one ? 1 : sh.per_cu2;
-  const size_t dyn = one ? sh.dyn1 : sh.dyn2;
+  // One workgroup per CU (one wave per SIMD): each tile carries enough
+  // matrix work for one wave to keep its loads flowing, ranges are as long
+  // as they can be (fewer pieces) and the staging areas as large. Two
+  // workgroups per CU, measured against it on MI355X, lose everywhere: the
+  // older workgroup's waves win the issue arbitration and finish their equal
+  // ranges well before the younger ones (MHA: 1.72 against 2.34 us per
+  // tile), so the launch ends on a long tail (MHA kernel 169 against 166 us;
+  // earlier, long split -3.9 %, GQA with a shared prefix -1.5 %, speculative
+  // verify -7.7 %, mixed step -2.5 %).
+  const size_t dyn = sh.dyn;
   // staging area per wave: what the prefix leaves, in whole 16-byte units.
   // Decode calls look for shared blocks when the first-block hash (at least
   // twice as many slots as sequences) and the sequences' slots fit there.
@@ -1097,7 +1080,7 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
       share_bits = bits;
   }
   // whole groups of num_kv_heads waves, no more than the GPU holds at once
-  int64_t waves = static_cast<int64_t>(sh.cus) * per_cu * waves_per_wg;
+  int64_t waves = static_cast<int64_t>(sh.cus) * waves_per_wg;
   int64_t per_kv = waves / a.num_kv_heads;
   if (per_kv < 1) per_kv = 1;
   const int64_t wgs = (per_kv * a.num_kv_heads + waves_per_wg - 1) / waves_per_wg;
