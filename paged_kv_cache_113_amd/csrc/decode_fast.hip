@@ -424,6 +424,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   __shared__ __attribute__((aligned(16))) char s_slots[(kSplitThreads / 64) * kSlotBytes];
   __shared__ int s_max[kSplitThreads / 64];
   __shared__ int s_wsum[kSplitThreads / 64];
+  __shared__ int s_ngroups;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -476,7 +477,23 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   };
 
   // 1. tiles per sequence and their exclusive prefix (every workgroup builds
-  //    the same table; it is tiny next to the KV stream)
+  //    the same table; it is tiny next to the KV stream). Each sequence's
+  //    tile count waits in its prefix entry until the scan is done; its first
+  //    block (for the shared-block detection further down) is read in the
+  //    same pass and kept in the staging areas, which are free until the
+  //    stream starts.
+  int* first_of = reinterpret_cast<int*>(reinterpret_cast<char*>(s_pre) +
+                                         ((static_cast<int>(sizeof(int)) * (S + 1) + 15) & ~15));
+  // first-block hash: slot = {first block, lowest holder, holders, highest
+  // holder}, then the list of the slots held more than once
+  const int H = 1 << share_bits;
+  int4* slots = reinterpret_cast<int4*>(reinterpret_cast<char*>(first_of) +
+                                        ((static_cast<int>(sizeof(int)) * S + 15) & ~15));
+  int* groups = reinterpret_cast<int*>(slots + H);   // [n_groups]
+  if (share_bits > 0) {
+    for (int i = tid; i < H; i += kSplitThreads) slots[i] = make_int4(-1, 0x7fffffff, 0, -1);
+    if (tid == 0) s_ngroups = 0;
+  }
   const int per = (S + kSplitThreads - 1) / kSplitThreads;
   const int s_lo = tid * per;
   int local = 0, nmax = 0;
@@ -484,7 +501,11 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     const int s = s_lo + i;
     if (s < S) {
       int last;
-      local += seq_tiles(s, last);
+      const int n = seq_tiles(s, last);
+      s_pre[s] = n;
+      if (share_bits > 0)
+        first_of[s] = read_only(a.block_table + static_cast<int64_t>(s) * a.max_blocks);
+      local += n;
       nmax = last > nmax ? last : nmax;
     }
   }
@@ -513,20 +534,14 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     T1 += s_wsum[i];
     n_max = s_max[i] > n_max ? s_max[i] : n_max;
   }
-  // (shared-block detection, below: each sequence's first block, kept in the
-  // staging areas, which are free until the stream starts)
-  int* first_of = reinterpret_cast<int*>(reinterpret_cast<char*>(s_pre) +
-                                         ((static_cast<int>(sizeof(int)) * (S + 1) + 15) & ~15));
   {
     int run = base + incl - local;  // exclusive prefix of this thread's chunk
     for (int i = 0; i < per; ++i) {
       const int s = s_lo + i;
       if (s < S) {
+        const int n = s_pre[s];
         s_pre[s] = run;
-        int last;
-        run += seq_tiles(s, last);
-        if (share_bits > 0)
-          first_of[s] = read_only(a.block_table + static_cast<int64_t>(s) * a.max_blocks);
+        run += n;
       }
     }
     if (tid == 0) s_pre[S] = T1;
@@ -542,100 +557,6 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     }
   }
   __syncthreads();
-  if (share_bits > 0 && T1 > 0) {
-    // first-block hash in the staging areas (free until the stream starts):
-    // slot = {first block, lowest holder, holders, highest holder}, then a
-    // list of the slots held more than once
-    const int H = 1 << share_bits;
-    int4* slots = reinterpret_cast<int4*>(reinterpret_cast<char*>(first_of) +
-                                          ((static_cast<int>(sizeof(int)) * S + 15) & ~15));
-    int* groups = reinterpret_cast<int*>(slots + H);   // [n_groups]
-    for (int i = tid; i < H; i += kSplitThreads) slots[i] = make_int4(-1, 0x7fffffff, 0, -1);
-    if (tid == 0) s_max[0] = 0;                        // group count
-    __syncthreads();
-    for (int i = 0; i < per; ++i) {
-      const int s = s_lo + i;
-      if (s >= S) break;
-      if (s_pre[s + 1] == s_pre[s]) continue;          // no positions
-      const int32_t b0 = first_of[s];
-      if (b0 < 0 || b0 >= a.num_blocks) continue;
-      int h = static_cast<int>(share_hash(b0, share_bits));
-      while (true) {
-        const int old = atomicCAS(&slots[h].x, -1, b0);
-        if (old == -1 || old == b0) break;
-        h = (h + 1) & (H - 1);
-      }
-      atomicMin(&slots[h].y, s);
-      atomicMax(&slots[h].w, s);
-      atomicAdd(&slots[h].z, 1);
-    }
-    __syncthreads();
-    for (int h = tid; h < H; h += kSplitThreads)
-      if (slots[h].z > 1) groups[atomicAdd(&s_max[0], 1)] = h;
-    __syncthreads();
-    const int n_groups = s_max[0];
-    const int n_wg = gridDim.x;
-    if (n_groups > 0 && n_wg % kXcds == 0) {
-      // a group's run: the leading blocks its lowest and highest holders
-      // have in common, within both contexts; one wave per group, 64 blocks
-      // compared at a time (into .x)
-      for (int g = w; g < n_groups; g += kSplitThreads / 64) {
-        const int h = groups[g];
-        const int r0 = slots[h].y, r1 = slots[h].w;
-        const int n0 = (seq_ctx(r0) + a.block_size - 1) / a.block_size;
-        const int n1 = (seq_ctx(r1) + a.block_size - 1) / a.block_size;
-        const int lim = n0 < n1 ? n0 : n1;
-        const int32_t* row0 = a.block_table + static_cast<int64_t>(r0) * a.max_blocks;
-        const int32_t* row1 = a.block_table + static_cast<int64_t>(r1) * a.max_blocks;
-        int run = 0;
-        for (int c0 = 0; c0 < lim; c0 += 64) {
-          const int b = c0 + lane;
-          bool same = false;
-          if (b < lim) {
-            const int32_t x0 = row0[b];
-            same = x0 == row1[b] && x0 >= 0 && x0 < a.num_blocks;
-          }
-          const uint64_t diff = ~__ballot(same);
-          if (diff != 0) {
-            run = c0 + static_cast<int>(__builtin_ctzll(diff));
-            break;
-          }
-          run = c0 + 64;
-        }
-        run = run < lim ? run : lim;
-        if (lane == 0) slots[h].x = run;
-      }
-      __syncthreads();
-      // every line of every run, spread over the workgroups of this XCD
-      // (workgroup i runs on XCD i % 8)
-      const int J = n_wg / kXcds;
-      const int j = blockIdx.x / kXcds;
-      const int lpb = a.block_size * kD * 2 / 128;           // lines per (block, head) slab
-      const int64_t head_stride = static_cast<int64_t>(a.block_size) * kD * 2;
-      const int64_t block_stride = head_stride * a.num_kv_heads;
-      const int per_blk = a.num_kv_heads * 2 * lpb;          // lines per block, K and V
-      uint32_t sink = 0;
-      for (int g = 0; g < n_groups; ++g) {
-        const int h = groups[g];
-        const int run = slots[h].x;
-        const int32_t* row = a.block_table + static_cast<int64_t>(slots[h].y) * a.max_blocks;
-        const int lines = run * per_blk;
-        for (int e = j * kSplitThreads + tid; e < lines; e += J * kSplitThreads) {
-          const int ib = e / per_blk;
-          const int r = e % per_blk;
-          const int kvh = r / (2 * lpb);
-          const int kv = (r / lpb) & 1;
-          const int64_t off = static_cast<int64_t>(row[ib]) * block_stride + kvh * head_stride +
-                              static_cast<int64_t>(r % lpb) * 128;
-          sink += *reinterpret_cast<const volatile uint32_t*>(
-              static_cast<const char*>(kv ? a.v_cache : a.k_cache) + off);
-        }
-      }
-      // keeps the loads (the sum means nothing)
-      if (sink == 0x9e3779b9u) s_wsum[0] = static_cast<int>(sink);
-    }
-    __syncthreads();
-  }
   if (T1 == 0) return;
 
   // 2. this wave's KV head and range of the stream. Workgroups are dealt to
@@ -660,9 +581,14 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     Wk = 1;
   }
   Wk = Wk < 1 ? 1 : Wk;
-  if (k >= Wk) return;
-  const int b0 = static_cast<int>(static_cast<int64_t>(k) * T1 / Wk);
-  const int b1 = static_cast<int>(static_cast<int64_t>(k + 1) * T1 / Wk);
+  // waves past Wk have no range of their own: they take the last range's
+  // bounds to stay well-formed, load nothing, and leave after the
+  // shared-block detection (whose barriers count every wave of the
+  // workgroup)
+  const bool active = k < Wk;
+  const int kr = active ? k : static_cast<int>(Wk) - 1;
+  const int b0 = static_cast<int>(static_cast<int64_t>(kr) * T1 / Wk);
+  const int b1 = static_cast<int>(static_cast<int64_t>(kr + 1) * T1 / Wk);
   const int len = b1 - b0;  // >= 1 since Wk <= T1
   // range holding stream tile x: largest r with floor(r*T1/Wk) <= x
   auto range_of = [&](int x) {
@@ -703,7 +629,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     }
     cur.t = x;
   }
-  int piece = k - range_of(ustart);  // index of this wave's piece of the unit
+  int piece = kr - range_of(ustart);  // index of this wave's piece of the unit
 
   auto advance = [&](const Cursor& c) {
     Cursor r = c;
@@ -956,13 +882,104 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
       }
     }
   };
+  // The shared-block detection runs once this wave's first tile loads are in
+  // flight: its hash work, run comparison and touches then sit in the
+  // tile's latency instead of delaying the tile's issue. (Its barriers wait
+  // for LDS work only: no global store of the compiler's is pending here.)
+  auto detect_shared = [&]() {
+    if (share_bits == 0) return;
+    for (int i = 0; i < per; ++i) {
+      const int s = s_lo + i;
+      if (s >= S) break;
+      if (s_pre[s + 1] == s_pre[s]) continue;          // no positions
+      const int32_t fb = first_of[s];
+      if (fb < 0 || fb >= a.num_blocks) continue;
+      int h = static_cast<int>(share_hash(fb, share_bits));
+      while (true) {
+        const int old = atomicCAS(&slots[h].x, -1, fb);
+        if (old == -1 || old == fb) break;
+        h = (h + 1) & (H - 1);
+      }
+      atomicMin(&slots[h].y, s);
+      atomicMax(&slots[h].w, s);
+      atomicAdd(&slots[h].z, 1);
+    }
+    __syncthreads();
+    for (int h = tid; h < H; h += kSplitThreads)
+      if (slots[h].z > 1) groups[atomicAdd(&s_ngroups, 1)] = h;
+    __syncthreads();
+    const int n_groups = s_ngroups;
+    const int n_wg = gridDim.x;
+    if (n_groups > 0 && n_wg % kXcds == 0) {
+      // a group's run: the leading blocks its lowest and highest holders
+      // have in common, within both contexts; one wave per group, 64 blocks
+      // compared at a time (into .x)
+      for (int g = w; g < n_groups; g += kSplitThreads / 64) {
+        const int h = groups[g];
+        const int r0 = slots[h].y, r1 = slots[h].w;
+        const int n0 = (seq_ctx(r0) + a.block_size - 1) / a.block_size;
+        const int n1 = (seq_ctx(r1) + a.block_size - 1) / a.block_size;
+        const int lim = n0 < n1 ? n0 : n1;
+        const int32_t* row0 = a.block_table + static_cast<int64_t>(r0) * a.max_blocks;
+        const int32_t* row1 = a.block_table + static_cast<int64_t>(r1) * a.max_blocks;
+        int run = 0;
+        for (int c0 = 0; c0 < lim; c0 += 64) {
+          const int b = c0 + lane;
+          bool same = false;
+          if (b < lim) {
+            const int32_t x0 = row0[b];
+            same = x0 == row1[b] && x0 >= 0 && x0 < a.num_blocks;
+          }
+          const uint64_t diff = ~__ballot(same);
+          if (diff != 0) {
+            run = c0 + static_cast<int>(__builtin_ctzll(diff));
+            break;
+          }
+          run = c0 + 64;
+        }
+        run = run < lim ? run : lim;
+        if (lane == 0) slots[h].x = run;
+      }
+      __syncthreads();
+      // every line of every run, spread over the workgroups of this XCD
+      // (workgroup i runs on XCD i % 8)
+      const int J = n_wg / kXcds;
+      const int j = blockIdx.x / kXcds;
+      const int lpb = a.block_size * kD * 2 / 128;           // lines per (block, head) slab
+      const int64_t head_stride = static_cast<int64_t>(a.block_size) * kD * 2;
+      const int64_t block_stride = head_stride * a.num_kv_heads;
+      const int per_blk = a.num_kv_heads * 2 * lpb;          // lines per block, K and V
+      uint32_t sink = 0;
+      for (int g = 0; g < n_groups; ++g) {
+        const int h = groups[g];
+        const int run = slots[h].x;
+        const int32_t* row = a.block_table + static_cast<int64_t>(slots[h].y) * a.max_blocks;
+        const int lines = run * per_blk;
+        for (int e = j * kSplitThreads + tid; e < lines; e += J * kSplitThreads) {
+          const int ib = e / per_blk;
+          const int r = e % per_blk;
+          const int hh = r / (2 * lpb);
+          const int kv = (r / lpb) & 1;
+          const int64_t off = static_cast<int64_t>(row[ib]) * block_stride + hh * head_stride +
+                              static_cast<int64_t>(r % lpb) * 128;
+          sink += *reinterpret_cast<const volatile uint32_t*>(
+              static_cast<const char*>(kv ? a.v_cache : a.k_cache) + off);
+        }
+      }
+      // keeps the loads (the sum means nothing)
+      if (sink == 0x9e3779b9u) s_wsum[0] = static_cast<int>(sink);
+    }
+    __syncthreads();
+  };
   // when this range starts with such a tile, the store must come first;
   // otherwise the first tile's loads go out first
   const bool append = !kVar && a.k_new != nullptr;
-  const bool first_is_new = append && pre(cur.s + 1) - 1 == b0;
+  const bool first_is_new = append && active && pre(cur.s + 1) - 1 == b0;
   if (first_is_new) append_new_tokens();
-  bool ga = geo.load(ta, row_of(cur.s), cur.t * kTile, kvh);
-  if (append && !first_is_new) append_new_tokens();
+  bool ga = active && geo.load(ta, row_of(cur.s), cur.t * kTile, kvh);
+  detect_shared();
+  if (append && active && !first_is_new) append_new_tokens();
+  if (!active) return;
   bool gb = true;
   Cursor nx = cur;
   int i = 0;
