@@ -858,27 +858,93 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   // range goes into the pool here, for this wave's KV head, by the wave that
   // reads that tile (the only reader of that row in this launch): its later
   // load of the tile comes after the store from the same wave, so it sees
-  // the new row. Lanes 0-15 store the K row's 16-byte chunks, lanes 16-31 the
-  // V row's, for up to two sequences per round (lanes 32-63).
-  auto append_new_tokens = [&]() {
-    const int b1 = b0 + len;
-    const int half = lane >> 5;
-    const int which = (lane >> 4) & 1;
-    const int chunk = lane & 15;
-    const char* src_base = static_cast<const char*>(which ? a.v_new : a.k_new);
-    char* dst_base = const_cast<char*>(which ? geo.vc : geo.kc);
-    for (int s0 = lo; s0 < S && pre(s0) < b1; s0 += 2) {
-      const int s = s0 + half;
-      if (s < S && s_pre[s + 1] > s_pre[s] && s_pre[s + 1] - 1 >= b0 && s_pre[s + 1] - 1 < b1) {
-        const int p = seq_ctx(s) - 1;
-        const int64_t blk = physical_block(row_of(s), p, a.block_size, a.max_blocks,
-                                           a.num_blocks);
-        const uint4 x = *reinterpret_cast<const uint4*>(
-            src_base + ((static_cast<int64_t>(s) * a.num_kv_heads + kvh) * kD) * 2 + chunk * 16);
-        if (blk >= 0)
-          store_untracked(dst_base + blk * geo.block_stride + kvh * geo.head_stride +
-                              static_cast<int64_t>(p % a.block_size) * kD * 2 + chunk * 16,
-                          x);
+  // the new row. Four tokens at a time: lane group g (16 lanes) moves token
+  // g's K and V rows, one 16-byte chunk of each per lane. The sequences are
+  // wave-uniform, so their slots come from scalar loads, which never wait
+  // for the wave's tile loads in flight.
+  const int g4 = lane >> 4;
+  const int c16 = lane & 15;
+  // lane i: does sequence s0 + i end in this range?
+  auto ends_in_range = [&](int s0) {
+    const int s = s0 + lane;
+    bool f = false;
+    if (s < S) {
+      const int t0 = s_pre[s], t1 = s_pre[s + 1];
+      f = t1 > t0 && t1 - 1 >= b0 && t1 - 1 < b1;
+    }
+    return static_cast<uint64_t>(__ballot(f));
+  };
+  // the sequence of the n-th set bit of m (uniform), -1 past the last
+  auto nth_seq = [&](int s0, uint64_t m, int n) {
+    for (int i = 0; i < n && m != 0; ++i) m &= m - 1;
+    return m != 0 ? s0 + static_cast<int>(__builtin_ctzll(m)) : -1;
+  };
+  auto pick4 = [&](int x0, int x1, int x2, int x3) {
+    return g4 == 0 ? x0 : g4 == 1 ? x1 : g4 == 2 ? x2 : x3;
+  };
+
+  // this lane's chunks of sequence s's new K and V rows
+  auto load_new = [&](int s, uint4& kx, uint4& vx) {
+    const int64_t src = ((static_cast<int64_t>(s) * a.num_kv_heads + kvh) * kD) * 2 + c16 * 16;
+    kx = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src);
+    vx = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src);
+  };
+  // Slots of four sequences' new rows, lane u < 4 for the u-th: its context
+  // length, then its table entry, one vector load each for all four; the
+  // byte offset of the row in this KV head's pools goes to lane group u (-1
+  // for no sequence, or no valid block there). A missing sequence reads
+  // sequence 0's entries and is dropped.
+  struct NewRows {
+    int xu;     // lane u: the sequence, or -1
+    int c;      // its context length
+    int32_t e;  // its last position's table entry
+  };
+  auto rows_ctx = [&](int x0, int x1, int x2, int x3) {
+    NewRows r;
+    r.xu = lane == 0 ? x0 : lane == 1 ? x1 : lane == 2 ? x2 : lane == 3 ? x3 : -1;
+    r.c = a.context_lens[r.xu >= 0 ? r.xu : 0];
+    r.e = -1;
+    return r;
+  };
+  auto last_pos = [&](const NewRows& r) { return (r.c < cap ? r.c : cap) - 1; };
+  auto rows_entry = [&](NewRows& r) {
+    const int p = last_pos(r);
+    r.e = row_of(r.xu >= 0 ? r.xu : 0)[p >= 0 ? p / a.block_size : 0];
+  };
+  auto rows_offset = [&](const NewRows& r) -> int64_t {
+    const int p = last_pos(r);
+    const int64_t o = r.xu >= 0 && p >= 0 && r.e >= 0 && r.e < a.num_blocks
+                          ? static_cast<int64_t>(r.e) * geo.block_stride +
+                                kvh * geo.head_stride +
+                                static_cast<int64_t>(p % a.block_size) * kD * 2
+                          : -1;
+    const int lo32 = __shfl(static_cast<int>(o & 0xffffffff), g4, 64);
+    const int hi32 = __shfl(static_cast<int>(o >> 32), g4, 64);
+    return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi32)) << 32) |
+                                static_cast<uint32_t>(lo32));
+  };
+  auto store_new = [&](int64_t off, const uint4& kx, const uint4& vx) {
+    if (off >= 0) {
+      store_untracked(const_cast<char*>(geo.kc) + off + c16 * 16, kx);
+      store_untracked(const_cast<char*>(geo.vc) + off + c16 * 16, vx);
+    }
+  };
+  // every token of the range but the first `skip` of the first window
+  auto append_rest = [&](int skip) {
+    for (int s0 = lo; s0 < S && pre(s0) < b1; s0 += 64) {
+      uint64_t m = ends_in_range(s0);
+      for (int i = 0; s0 == lo && i < skip && m != 0; ++i) m &= m - 1;
+      while (m != 0) {
+        const int x0 = nth_seq(s0, m, 0), x1 = nth_seq(s0, m, 1);
+        const int x2 = nth_seq(s0, m, 2), x3 = nth_seq(s0, m, 3);
+        const int my = pick4(x0, x1, x2, x3);
+        uint4 kx = make_uint4(0, 0, 0, 0), vx = kx;
+        if (my >= 0) load_new(my, kx, vx);
+        NewRows r = rows_ctx(x0, x1, x2, x3);
+        rows_entry(r);
+        const int64_t o = rows_offset(r);
+        if (my >= 0) store_new(o, kx, vx);
+        for (int i = 0; i < 4 && m != 0; ++i) m &= m - 1;
       }
     }
   };
@@ -949,21 +1015,40 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
       const int64_t head_stride = static_cast<int64_t>(a.block_size) * kD * 2;
       const int64_t block_stride = head_stride * a.num_kv_heads;
       const int per_blk = a.num_kv_heads * 2 * lpb;          // lines per block, K and V
+      // Four lines per thread per round: their table entries, then their
+      // loads, all in flight together (plain loads, which keep the lines in
+      // the XCD's cache).
+      constexpr int kTouch = 4;
       uint32_t sink = 0;
       for (int g = 0; g < n_groups; ++g) {
         const int h = groups[g];
         const int run = slots[h].x;
         const int32_t* row = a.block_table + static_cast<int64_t>(slots[h].y) * a.max_blocks;
         const int lines = run * per_blk;
-        for (int e = j * kSplitThreads + tid; e < lines; e += J * kSplitThreads) {
-          const int ib = e / per_blk;
-          const int r = e % per_blk;
-          const int hh = r / (2 * lpb);
-          const int kv = (r / lpb) & 1;
-          const int64_t off = static_cast<int64_t>(row[ib]) * block_stride + hh * head_stride +
-                              static_cast<int64_t>(r % lpb) * 128;
-          sink += *reinterpret_cast<const volatile uint32_t*>(
-              static_cast<const char*>(kv ? a.v_cache : a.k_cache) + off);
+        for (int e0 = j * kSplitThreads * kTouch + tid; e0 < lines;
+             e0 += J * kSplitThreads * kTouch) {
+          int32_t blk[kTouch];
+#pragma unroll
+          for (int u = 0; u < kTouch; ++u) {
+            const int e = e0 + u * kSplitThreads;
+            blk[u] = e < lines ? row[e / per_blk] : -1;
+          }
+#pragma unroll
+          for (int u = 0; u < kTouch; ++u) {
+            const int e = e0 + u * kSplitThreads;
+            const int r = e % per_blk;
+            const int hh = r / (2 * lpb);
+            const int kv = (r / lpb) & 1;
+            const bool ok = e < lines && blk[u] >= 0 && blk[u] < a.num_blocks;
+            // (no branch around the load: the four stay in flight together;
+            // a line out of range reads the pool's first line instead)
+            const int64_t off = ok ? static_cast<int64_t>(blk[u]) * block_stride +
+                                         hh * head_stride + static_cast<int64_t>(r % lpb) * 128
+                                   : 0;
+            const uint32_t x = *reinterpret_cast<const uint32_t*>(
+                static_cast<const char*>(kv ? a.v_cache : a.k_cache) + off);
+            sink += ok ? x : 0u;
+          }
         }
       }
       // keeps the loads (the sum means nothing)
@@ -971,14 +1056,41 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     }
     __syncthreads();
   };
-  // when this range starts with such a tile, the store must come first;
-  // otherwise the first tile's loads go out first
-  const bool append = !kVar && a.k_new != nullptr;
-  const bool first_is_new = append && active && pre(cur.s + 1) - 1 == b0;
-  if (first_is_new) append_new_tokens();
-  bool ga = active && geo.load(ta, row_of(cur.s), cur.t * kTile, kvh);
+  // When this range starts with a sequence's last tile, every store comes
+  // before the first tile's loads. Otherwise the first four tokens' rows are
+  // loaded before the tile (so waiting for them does not wait for it), the
+  // tile's loads go out, then their stores; the rest follow the shared-block
+  // detection.
+  const bool append = !kVar && a.k_new != nullptr && active;
+  const bool first_is_new = append && pre(cur.s + 1) - 1 == b0;
+  if (first_is_new) append_rest(0);
+  const bool early = append && !first_is_new;
+  uint64_t m_new = 0;
+  int xa = -1, xb = -1, xc = -1, xd = -1, x_my = -1;
+  uint4 k_my = make_uint4(0, 0, 0, 0), v_my = k_my;
+  NewRows r_new{-1, 0, -1};
+  if (early) {
+    m_new = ends_in_range(lo);
+    xa = nth_seq(lo, m_new, 0);
+    xb = nth_seq(lo, m_new, 1);
+    xc = nth_seq(lo, m_new, 2);
+    xd = nth_seq(lo, m_new, 3);
+    x_my = pick4(xa, xb, xc, xd);
+    if (x_my >= 0) load_new(x_my, k_my, v_my);
+    r_new = rows_ctx(xa, xb, xc, xd);
+  }
+  // (an idle wave loads its stand-in range's first tile too: a branch here
+  // would make every later wait on this path count as if the loads were
+  // absent, and wait for the tile itself)
+  bool ga = geo.load(ta, row_of(cur.s), cur.t * kTile, kvh);
+  if (early) rows_entry(r_new);
   detect_shared();
-  if (append && active && !first_is_new) append_new_tokens();
+  if (early) {
+    const int64_t o = rows_offset(r_new);  // (every lane: a cross-lane read)
+    if (x_my >= 0) store_new(o, k_my, v_my);
+  }
+  if (early && (__builtin_popcountll(m_new) > 4 || (lo + 64 < S && pre(lo + 64) < b1)))
+    append_rest(4);
   if (!active) return;
   bool gb = true;
   Cursor nx = cur;
