@@ -948,12 +948,13 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
       }
     }
   };
-  // The shared-block detection runs once this wave's first tile loads are in
-  // flight: its hash work, run comparison and touches then sit in the
-  // tile's latency instead of delaying the tile's issue. (Its barriers wait
-  // for LDS work only: no global store of the compiler's is pending here.)
-  auto detect_shared = [&]() {
-    if (share_bits == 0) return;
+  // Shared-block detection, in two parts. Finding the groups is LDS work
+  // only. Their runs' lines are touched before this wave's first tile loads
+  // go out, so that a wave whose range starts inside a shared run finds
+  // them in its XCD's cache; the touches' own results are waited for after
+  // the tile's loads are issued.
+  auto find_groups = [&]() -> int {
+    if (share_bits == 0) return 0;
     for (int i = 0; i < per; ++i) {
       const int s = s_lo + i;
       if (s >= S) break;
@@ -974,7 +975,10 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     for (int h = tid; h < H; h += kSplitThreads)
       if (slots[h].z > 1) groups[atomicAdd(&s_ngroups, 1)] = h;
     __syncthreads();
-    const int n_groups = s_ngroups;
+    return s_ngroups;
+  };
+  auto touch_runs = [&](int n_groups) -> uint32_t {
+    uint32_t sink = 0;
     const int n_wg = gridDim.x;
     if (n_groups > 0 && n_wg % kXcds == 0) {
       // a group's run: the leading blocks its lowest and highest holders
@@ -1019,7 +1023,6 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
       // loads, all in flight together (plain loads, which keep the lines in
       // the XCD's cache).
       constexpr int kTouch = 4;
-      uint32_t sink = 0;
       for (int g = 0; g < n_groups; ++g) {
         const int h = groups[g];
         const int run = slots[h].x;
@@ -1051,16 +1054,16 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
           }
         }
       }
-      // keeps the loads (the sum means nothing)
-      if (sink == 0x9e3779b9u) s_wsum[0] = static_cast<int>(sink);
     }
-    __syncthreads();
+    return sink;
   };
   // When this range starts with a sequence's last tile, every store comes
   // before the first tile's loads. Otherwise the first four tokens' rows are
   // loaded before the tile (so waiting for them does not wait for it), the
   // tile's loads go out, then their stores; the rest follow the shared-block
   // detection.
+  const int n_groups = find_groups();
+  const uint32_t sink = touch_runs(n_groups);
   const bool append = !kVar && a.k_new != nullptr && active;
   const bool first_is_new = append && pre(cur.s + 1) - 1 == b0;
   if (first_is_new) append_rest(0);
@@ -1084,7 +1087,10 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   // absent, and wait for the tile itself)
   bool ga = geo.load(ta, row_of(cur.s), cur.t * kTile, kvh);
   if (early) rows_entry(r_new);
-  detect_shared();
+  // keeps the touches' loads (the sum means nothing); the barrier holds every
+  // wave's staging area until the workgroup is done with the group lists
+  if (sink == 0x9e3779b9u) s_wsum[0] = static_cast<int>(sink);
+  if (n_groups > 0) __syncthreads();
   if (early) {
     const int64_t o = rows_offset(r_new);  // (every lane: a cross-lane read)
     if (x_my >= 0) store_new(o, k_my, v_my);
