@@ -362,10 +362,10 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int s, int kvh
 // after its count, so it sees every piece whichever XCD wrote it. (A cache
 // write-back and invalidate per wave instead cost more than the merge
 // saves.)
-template <typename RangeOf>
+template <typename PiecesOf>
 __device__ __forceinline__ void merge_arrivals(const DecodeArgs& a, const int* s_pre, int S,
                                                int lo, int b0, int b1, int kvh, int G, int mp,
-                                               RangeOf range_of) {
+                                               PiecesOf pieces_of) {
   const int lane = threadIdx.x & 63;
   auto pre = [&](int s) { return __builtin_amdgcn_readfirstlane(s_pre[s]); };
   // the pieces' stores were issued as instructions the compiler does not
@@ -381,7 +381,7 @@ __device__ __forceinline__ void merge_arrivals(const DecodeArgs& a, const int* s
     if (s < S) {
       const int t0 = s_pre[s], t1 = s_pre[s + 1];
       if (t0 < b1 && t1 > b0 && t1 > t0) {
-        n = range_of(t1 - 1) - range_of(t0) + 1;
+        n = pieces_of(s, t0, t1);
         if (n > 1) {
           int32_t* ctr = a.counters + static_cast<int64_t>(s) * a.num_kv_heads + kvh;
           last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -411,6 +411,25 @@ __device__ __forceinline__ void merge_arrivals(const DecodeArgs& a, const int* s
 constexpr int kShareSlotBytes = 16;   // hash slot: key / run, lowest holder, count, another
 __device__ __forceinline__ uint32_t share_hash(int32_t b, int bits) {
   return (static_cast<uint32_t>(b) * 2654435761u) >> (32 - bits);
+}
+
+// Largest i in [0, n) with v[i] <= x, for v nondecreasing with v[0] <= x
+// (a prefix table in LDS), found by the whole wave: each round every lane
+// compares one of 64 evenly spaced entries, and the ballot (a prefix of the
+// lanes, v being sorted) narrows the interval to one step. Two rounds for up
+// to 4096 entries. The result is wave-uniform.
+__device__ __forceinline__ int last_le(const int* v, int n, int64_t x) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = n;  // the answer lies in [lo, hi)
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int i = lo + lane * step;
+    const bool le = i < hi && v[i] <= x;
+    const int cnt = __popcll(__ballot(le));  // >= 1: v[lo] <= x
+    lo += (cnt - 1) * step;
+    hi = lo + step < hi ? lo + step : hi;
+  }
+  return lo;
 }
 
 template <typename T, bool kVar>
@@ -482,8 +501,12 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   //    block (for the shared-block detection further down) is read in the
   //    same pass and kept in the staging areas, which are free until the
   //    stream starts.
-  int* first_of = reinterpret_cast<int*>(reinterpret_cast<char*>(s_pre) +
-                                         ((static_cast<int>(sizeof(int)) * (S + 1) + 15) & ~15));
+  // (with shared-block detection a second prefix, of costs, follows the
+  // first: see step 3)
+  const int pre_ints = (S + 1 + 3) & ~3;
+  int* s_cost = s_pre + pre_ints;
+  char* stage_base = reinterpret_cast<char*>(s_pre + pre_ints * (share_bits > 0 ? 2 : 1));
+  int* first_of = reinterpret_cast<int*>(stage_base);
   // first-block hash: slot = {first block, lowest holder, holders, highest
   // holder}, then the list of the slots held more than once
   const int H = 1 << share_bits;
@@ -559,14 +582,192 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   __syncthreads();
   if (T1 == 0) return;
 
-  // 2. this wave's KV head and range of the stream. Workgroups are dealt to
+  // 2. Shared runs (blocks several sequences hold at the same logical index,
+  //    found by the sequences' first blocks: see share_hash): the groups are
+  //    found in LDS, then each group's run is measured in the table.
+  auto find_groups = [&]() -> int {
+    if (share_bits == 0) return 0;
+    for (int i = 0; i < per; ++i) {
+      const int s = s_lo + i;
+      if (s >= S) break;
+      if (s_pre[s + 1] == s_pre[s]) continue;          // no positions
+      const int32_t fb = first_of[s];
+      if (fb < 0 || fb >= a.num_blocks) continue;
+      int h = static_cast<int>(share_hash(fb, share_bits));
+      while (true) {
+        const int old = atomicCAS(&slots[h].x, -1, fb);
+        if (old == -1 || old == fb) break;
+        h = (h + 1) & (H - 1);
+      }
+      atomicMin(&slots[h].y, s);
+      atomicMax(&slots[h].w, s);
+      atomicAdd(&slots[h].z, 1);
+    }
+    __syncthreads();
+    for (int h = tid; h < H; h += kSplitThreads)
+      if (slots[h].z > 1) groups[atomicAdd(&s_ngroups, 1)] = h;
+    __syncthreads();
+    return s_ngroups;
+  };
+  const int n_wg = gridDim.x;
+  const int n_groups = find_groups();
+  const bool touched = n_groups > 0 && n_wg % kXcds == 0;
+  if (touched) {
+    // a group's run: the leading blocks its lowest and highest holders have
+    // in common, within both contexts; one wave per group, 64 blocks
+    // compared at a time (into .z, as -run - 1: the holder count is no
+    // longer needed)
+    for (int g = w; g < n_groups; g += kSplitThreads / 64) {
+      const int h = groups[g];
+      const int r0 = slots[h].y, r1 = slots[h].w;
+      const int n0 = (seq_ctx(r0) + a.block_size - 1) / a.block_size;
+      const int n1 = (seq_ctx(r1) + a.block_size - 1) / a.block_size;
+      const int lim = n0 < n1 ? n0 : n1;
+      const int32_t* row0 = a.block_table + static_cast<int64_t>(r0) * a.max_blocks;
+      const int32_t* row1 = a.block_table + static_cast<int64_t>(r1) * a.max_blocks;
+      int run = 0;
+      for (int c0 = 0; c0 < lim; c0 += 64) {
+        const int b = c0 + lane;
+        bool same = false;
+        if (b < lim) {
+          const int32_t x0 = row0[b];
+          same = x0 == row1[b] && x0 >= 0 && x0 < a.num_blocks;
+        }
+        const uint64_t diff = ~__ballot(same);
+        if (diff != 0) {
+          run = c0 + static_cast<int>(__builtin_ctzll(diff));
+          break;
+        }
+        run = c0 + 64;
+      }
+      run = run < lim ? run : lim;
+      if (lane == 0) slots[h].z = -run - 1;
+    }
+    __syncthreads();
+  }
+  // The shared runs' lines are touched now, well before this wave's first
+  // tile loads go out, so that a wave whose range starts inside a shared run
+  // finds them in its XCD's cache; the touches' own results are waited for
+  // after the tile's loads are issued.
+  constexpr int kTouch = 4;
+  uint32_t sink = 0;
+  uint32_t last_touch[kTouch] = {0u, 0u, 0u, 0u};
+  auto touch_runs = [&](int n_groups) {
+    if (n_groups > 0 && n_wg % kXcds == 0) {
+      // every line of every run, spread over the workgroups of this XCD
+      // (workgroup i runs on XCD i % 8)
+      const int J = n_wg / kXcds;
+      const int j = blockIdx.x / kXcds;
+      const int lpb = a.block_size * kD * 2 / 128;           // lines per (block, head) slab
+      const int64_t head_stride = static_cast<int64_t>(a.block_size) * kD * 2;
+      const int64_t block_stride = head_stride * a.num_kv_heads;
+      const int per_blk = a.num_kv_heads * 2 * lpb;          // lines per block, K and V
+      // Four lines per thread per round: their table entries, then their
+      // loads, all in flight together (plain loads, which keep the lines in
+      // the XCD's cache). A round's values are summed in the next round, the
+      // last round's after the first tile's loads are issued, so no wait
+      // for them stands before those loads.
+      for (int g = 0; g < n_groups; ++g) {
+        const int h = groups[g];
+        const int run = -slots[h].z - 1;
+        const int32_t* row = a.block_table + static_cast<int64_t>(slots[h].y) * a.max_blocks;
+        const int lines = run * per_blk;
+        for (int e0 = j * kSplitThreads * kTouch + tid; e0 < lines;
+             e0 += J * kSplitThreads * kTouch) {
+          int32_t blk[kTouch];
+#pragma unroll
+          for (int u = 0; u < kTouch; ++u) {
+            const int e = e0 + u * kSplitThreads;
+            blk[u] = e < lines ? row[e / per_blk] : -1;
+          }
+#pragma unroll
+          for (int u = 0; u < kTouch; ++u) {
+            const int e = e0 + u * kSplitThreads;
+            const int r = e % per_blk;
+            const int hh = r / (2 * lpb);
+            const int kv = (r / lpb) & 1;
+            const bool ok = e < lines && blk[u] >= 0 && blk[u] < a.num_blocks;
+            // (no branch around the load: the four stay in flight together;
+            // a line out of range reads the pool's first line instead)
+            const int64_t off = ok ? static_cast<int64_t>(blk[u]) * block_stride +
+                                         hh * head_stride + static_cast<int64_t>(r % lpb) * 128
+                                   : 0;
+            sink += last_touch[u];
+            last_touch[u] = *reinterpret_cast<const uint32_t*>(
+                static_cast<const char*>(kv ? a.v_cache : a.k_cache) + off);
+          }
+        }
+      }
+    }
+  };
+  touch_runs(n_groups);
+
+  // 3. The split balances work, not tiles. Without shared runs every tile
+  //    is one unit. With them, a tile of a sharer's shared run costs 3 and
+  //    any other tile 4: the runs are touched into each XCD's cache before
+  //    the stream, and a wave reads such a tile in about three quarters of
+  //    the time of a tile from HBM (0.84 against 1.12 us measured), so
+  //    waves whose ranges hold shared tiles take more tiles. s_cost is the
+  //    exclusive prefix of the costs per sequence (the shared tiles of a
+  //    sequence lead it, so a sequence's cost and tile count give both).
+  const bool weighted = touched && static_cast<int64_t>(T1) * 4 < 0x7fffffff;
+  int64_t C = T1;
+  if (weighted) {
+    const int tiles_per_block = a.block_size / kTile;
+    int lc = 0;
+    for (int i = 0; i < per; ++i) {
+      const int s = s_lo + i;
+      if (s < S) {
+        const int n = s_pre[s + 1] - s_pre[s];
+        int sh = 0;
+        const int32_t fb = first_of[s];
+        if (n > 0 && fb >= 0 && fb < a.num_blocks) {
+          int h = static_cast<int>(share_hash(fb, share_bits));
+          while (slots[h].x != fb && slots[h].x != -1) h = (h + 1) & (H - 1);
+          const int z = slots[h].x == fb ? slots[h].z : 1;
+          sh = z < 0 ? (-z - 1) * tiles_per_block : 0;
+          sh = sh < n ? sh : n;
+        }
+        s_cost[s] = 4 * n - sh;
+        lc += 4 * n - sh;
+      }
+    }
+    int ci = lc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(ci, off, 64);
+      if (lane >= off) ci += y;
+    }
+    if (lane == 63) s_wsum[w] = ci;
+    __syncthreads();
+    int cbase = 0, ctot = 0;
+#pragma unroll
+    for (int i = 0; i < kSplitThreads / 64; ++i) {
+      cbase += i < w ? s_wsum[i] : 0;
+      ctot += s_wsum[i];
+    }
+    int run = cbase + ci - lc;
+    for (int i = 0; i < per; ++i) {
+      const int s = s_lo + i;
+      if (s < S) {
+        const int c = s_cost[s];
+        s_cost[s] = run;
+        run += c;
+      }
+    }
+    if (tid == 0) s_cost[S] = ctot;
+    C = ctot;
+    __syncthreads();
+  }
+
+  // 4. this wave's KV head and range of the stream. Workgroups are dealt to
   //    the 8 XCDs round-robin (workgroup i runs on XCD i % 8); numbering the
   //    waves XCD by XCD gives each XCD a contiguous run of ranges over all KV
   //    heads, so the heads of a block are read side by side on one XCD.
   //    Ranges hold at least q_min tiles so that no unit is cut into more
   //    than max_partitions pieces: a unit of n tiles meets at most
-  //    ceil((n-1)/q_min) + 1.
-  const int n_wg = gridDim.x;
+  //    ceil((n-1)/q_min) + 1 (weighted, a range of cost C/Wk >= 4 q_min
+  //    holds at least q_min tiles: a tile costs at most 4).
   const int xcd_rank = (blockIdx.x % kXcds) * (n_wg / kXcds) + blockIdx.x / kXcds;
   const int wg_rank = n_wg % kXcds == 0 ? xcd_rank : static_cast<int>(blockIdx.x);
   const int gw = wg_rank * (kSplitThreads / 64) + w;
@@ -575,35 +776,47 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   int64_t Wk = waves_per_kv;
   if (mp >= 2) {
     const int q_min = n_max > 1 ? (n_max - 1 + mp - 2) / (mp - 1) : 1;
-    const int64_t lim = T1 / q_min;
+    const int64_t lim = weighted ? C / (4 * q_min) : T1 / q_min;
     Wk = Wk < lim ? Wk : lim;
   } else {
     Wk = 1;
   }
   Wk = Wk < 1 ? 1 : Wk;
   // waves past Wk have no range of their own: they take the last range's
-  // bounds to stay well-formed, load nothing, and leave after the
-  // shared-block detection (whose barriers count every wave of the
-  // workgroup)
+  // bounds to stay well-formed, store nothing, and leave after the shared
+  // runs' touches (whose barrier counts every wave of the workgroup)
   const bool active = k < Wk;
   const int kr = active ? k : static_cast<int>(Wk) - 1;
-  const int b0 = static_cast<int>(static_cast<int64_t>(kr) * T1 / Wk);
-  const int b1 = static_cast<int>(static_cast<int64_t>(kr + 1) * T1 / Wk);
-  const int len = b1 - b0;  // >= 1 since Wk <= T1
-  // range holding stream tile x: largest r with floor(r*T1/Wk) <= x
-  auto range_of = [&](int x) {
-    return static_cast<int>(((static_cast<int64_t>(x) + 1) * Wk - 1) / T1);
-  };
 
   // LDS reads come back in VGPRs; the prefix is the same for every lane, and
   // saying so keeps the cursor, table reads and tile addresses scalar
   auto pre = [&](int s) { return __builtin_amdgcn_readfirstlane(s_pre[s]); };
+  auto cst = [&](int s) { return __builtin_amdgcn_readfirstlane(s_cost[s]); };
+  // Range r covers the tiles whose cost starts in [floor(r C / Wk),
+  // floor((r+1) C / Wk)); unweighted, a tile's cost start is its stream
+  // index. The range holding cost c: the largest r with floor(r C/Wk) <= c.
+  auto range_of_cost = [&](int64_t c) { return static_cast<int>(((c + 1) * Wk - 1) / C); };
+  // cost start of tile t of a sequence (per lane: c0 = its cost prefix, n its
+  // tiles, n_cost its cost; its shared tiles lead it)
+  auto cost_in = [](int64_t c0, int n, int n_cost, int t) -> int64_t {
+    const int sh = 4 * n - n_cost;
+    return c0 + (t < sh ? 3 * t : 3 * sh + 4 * (t - sh));
+  };
+  // first stream tile whose cost starts at c or later (wave-uniform)
+  auto tile_at = [&](int64_t c) -> int {
+    if (!weighted) return static_cast<int>(c);
+    if (c >= C) return T1;
+    const int l = last_le(s_cost, S, c);  // a sequence with tiles
+    const int n = pre(l + 1) - pre(l);
+    const int sh = 4 * n - (cst(l + 1) - cst(l));
+    const int r = static_cast<int>(c - cst(l));
+    return pre(l) + (r <= 3 * sh ? (r + 2) / 3 : sh + (r - 3 * sh + 3) / 4);
+  };
+  const int b0 = tile_at(static_cast<int64_t>(kr) * C / Wk);
+  const int b1 = tile_at(static_cast<int64_t>(kr + 1) * C / Wk);
+  const int len = b1 - b0;  // >= 1: Wk <= T1, or C/Wk >= 4
   // sequence holding tile b0: largest s with s_pre[s] <= b0
-  int lo = 0, hi = S - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pre(mid) <= b0) lo = mid; else hi = mid - 1;
-  }
+  const int lo = last_le(s_pre, S, b0);
   auto open_seq = [&](int s) {
     Cursor c;
     c.s = s;
@@ -629,7 +842,8 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     }
     cur.t = x;
   }
-  int piece = kr - range_of(ustart);  // index of this wave's piece of the unit
+  // index of this wave's piece of the unit (weighted: decode, unit = sequence)
+  int piece = kr - range_of_cost(weighted ? static_cast<int64_t>(cst(lo)) : ustart);
 
   auto advance = [&](const Cursor& c) {
     Cursor r = c;
@@ -715,8 +929,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   // Record: int4 header {sequence (decode) or first query row, column group,
   // slot, nl | mark << 16 | single << 17}, then nl rows of 128 floats, then
   // nl (m, l) pairs.
-  PKV_LDS char* stage = (PKV_LDS char*)(s_pre) +
-                        ((static_cast<int>(sizeof(int)) * (S + 1) + 15) & ~15) + w * stage_bytes;
+  PKV_LDS char* stage = (PKV_LDS char*)(stage_base) + w * stage_bytes;
   int st_used = 0, st_n = 0;  // bytes and records staged (wave-uniform)
   auto live_cols = [&](const Cursor& c) {
     if constexpr (kVar) {
@@ -948,122 +1161,11 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
       }
     }
   };
-  // Shared-block detection, in two parts. Finding the groups is LDS work
-  // only. Their runs' lines are touched before this wave's first tile loads
-  // go out, so that a wave whose range starts inside a shared run finds
-  // them in its XCD's cache; the touches' own results are waited for after
-  // the tile's loads are issued.
-  auto find_groups = [&]() -> int {
-    if (share_bits == 0) return 0;
-    for (int i = 0; i < per; ++i) {
-      const int s = s_lo + i;
-      if (s >= S) break;
-      if (s_pre[s + 1] == s_pre[s]) continue;          // no positions
-      const int32_t fb = first_of[s];
-      if (fb < 0 || fb >= a.num_blocks) continue;
-      int h = static_cast<int>(share_hash(fb, share_bits));
-      while (true) {
-        const int old = atomicCAS(&slots[h].x, -1, fb);
-        if (old == -1 || old == fb) break;
-        h = (h + 1) & (H - 1);
-      }
-      atomicMin(&slots[h].y, s);
-      atomicMax(&slots[h].w, s);
-      atomicAdd(&slots[h].z, 1);
-    }
-    __syncthreads();
-    for (int h = tid; h < H; h += kSplitThreads)
-      if (slots[h].z > 1) groups[atomicAdd(&s_ngroups, 1)] = h;
-    __syncthreads();
-    return s_ngroups;
-  };
-  auto touch_runs = [&](int n_groups) -> uint32_t {
-    uint32_t sink = 0;
-    const int n_wg = gridDim.x;
-    if (n_groups > 0 && n_wg % kXcds == 0) {
-      // a group's run: the leading blocks its lowest and highest holders
-      // have in common, within both contexts; one wave per group, 64 blocks
-      // compared at a time (into .x)
-      for (int g = w; g < n_groups; g += kSplitThreads / 64) {
-        const int h = groups[g];
-        const int r0 = slots[h].y, r1 = slots[h].w;
-        const int n0 = (seq_ctx(r0) + a.block_size - 1) / a.block_size;
-        const int n1 = (seq_ctx(r1) + a.block_size - 1) / a.block_size;
-        const int lim = n0 < n1 ? n0 : n1;
-        const int32_t* row0 = a.block_table + static_cast<int64_t>(r0) * a.max_blocks;
-        const int32_t* row1 = a.block_table + static_cast<int64_t>(r1) * a.max_blocks;
-        int run = 0;
-        for (int c0 = 0; c0 < lim; c0 += 64) {
-          const int b = c0 + lane;
-          bool same = false;
-          if (b < lim) {
-            const int32_t x0 = row0[b];
-            same = x0 == row1[b] && x0 >= 0 && x0 < a.num_blocks;
-          }
-          const uint64_t diff = ~__ballot(same);
-          if (diff != 0) {
-            run = c0 + static_cast<int>(__builtin_ctzll(diff));
-            break;
-          }
-          run = c0 + 64;
-        }
-        run = run < lim ? run : lim;
-        if (lane == 0) slots[h].x = run;
-      }
-      __syncthreads();
-      // every line of every run, spread over the workgroups of this XCD
-      // (workgroup i runs on XCD i % 8)
-      const int J = n_wg / kXcds;
-      const int j = blockIdx.x / kXcds;
-      const int lpb = a.block_size * kD * 2 / 128;           // lines per (block, head) slab
-      const int64_t head_stride = static_cast<int64_t>(a.block_size) * kD * 2;
-      const int64_t block_stride = head_stride * a.num_kv_heads;
-      const int per_blk = a.num_kv_heads * 2 * lpb;          // lines per block, K and V
-      // Four lines per thread per round: their table entries, then their
-      // loads, all in flight together (plain loads, which keep the lines in
-      // the XCD's cache).
-      constexpr int kTouch = 4;
-      for (int g = 0; g < n_groups; ++g) {
-        const int h = groups[g];
-        const int run = slots[h].x;
-        const int32_t* row = a.block_table + static_cast<int64_t>(slots[h].y) * a.max_blocks;
-        const int lines = run * per_blk;
-        for (int e0 = j * kSplitThreads * kTouch + tid; e0 < lines;
-             e0 += J * kSplitThreads * kTouch) {
-          int32_t blk[kTouch];
-#pragma unroll
-          for (int u = 0; u < kTouch; ++u) {
-            const int e = e0 + u * kSplitThreads;
-            blk[u] = e < lines ? row[e / per_blk] : -1;
-          }
-#pragma unroll
-          for (int u = 0; u < kTouch; ++u) {
-            const int e = e0 + u * kSplitThreads;
-            const int r = e % per_blk;
-            const int hh = r / (2 * lpb);
-            const int kv = (r / lpb) & 1;
-            const bool ok = e < lines && blk[u] >= 0 && blk[u] < a.num_blocks;
-            // (no branch around the load: the four stay in flight together;
-            // a line out of range reads the pool's first line instead)
-            const int64_t off = ok ? static_cast<int64_t>(blk[u]) * block_stride +
-                                         hh * head_stride + static_cast<int64_t>(r % lpb) * 128
-                                   : 0;
-            const uint32_t x = *reinterpret_cast<const uint32_t*>(
-                static_cast<const char*>(kv ? a.v_cache : a.k_cache) + off);
-            sink += ok ? x : 0u;
-          }
-        }
-      }
-    }
-    return sink;
-  };
   // When this range starts with a sequence's last tile, every store comes
   // before the first tile's loads. Otherwise the first four tokens' rows are
   // loaded before the tile (so waiting for them does not wait for it), the
   // tile's loads go out, then their stores; the rest follow the shared-block
   // detection.
-  const int n_groups = find_groups();
-  const uint32_t sink = touch_runs(n_groups);
   const bool append = !kVar && a.k_new != nullptr && active;
   const bool first_is_new = append && pre(cur.s + 1) - 1 == b0;
   if (first_is_new) append_rest(0);
@@ -1089,6 +1191,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   if (early) rows_entry(r_new);
   // keeps the touches' loads (the sum means nothing); the barrier holds every
   // wave's staging area until the workgroup is done with the group lists
+  sink += (last_touch[0] + last_touch[1]) + (last_touch[2] + last_touch[3]);
   if (sink == 0x9e3779b9u) s_wsum[0] = static_cast<int>(sink);
   if (n_groups > 0) __syncthreads();
   if (early) {
@@ -1130,8 +1233,12 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     if (!step(tb, gb, ta, ga)) break;
   }
   flush();
-  if (fused) merge_arrivals(a, s_pre, S, lo, b0, b0 + len, kvh, G, mp, [&](int x) {
-      return range_of(x);
+  // pieces of sequence s (per lane; t0, t1: its stream tiles)
+  if (fused) merge_arrivals(a, s_pre, S, lo, b0, b0 + len, kvh, G, mp, [&](int s, int t0, int t1) {
+      if (!weighted) return range_of_cost(t1 - 1) - range_of_cost(t0) + 1;
+      const int c0 = s_cost[s];
+      const int nc = s_cost[s + 1] - c0;
+      return range_of_cost(cost_in(c0, t1 - t0, nc, t1 - t0 - 1)) - range_of_cost(c0) + 1;
     });
 }
 
@@ -1200,20 +1307,23 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
   // earlier, long split -3.9 %, GQA with a shared prefix -1.5 %, speculative
   // verify -7.7 %, mixed step -2.5 %).
   const size_t dyn = sh.dyn;
-  // staging area per wave: what the prefix leaves, in whole 16-byte units.
-  // Decode calls look for shared blocks when the first-block hash (at least
-  // twice as many slots as sequences) and the sequences' slots fit there.
+  // Decode calls look for shared blocks when a second prefix (the costs of
+  // the weighted split) fits beside the first, and the sequences' first
+  // blocks and the first-block hash (at least twice as many slots as
+  // sequences) fit in the staging areas. Staging area per wave: what the
+  // prefixes leave, in whole 16-byte units.
   const size_t pre = (static_cast<size_t>(a.num_seqs + 1) * sizeof(int) + 15) & ~size_t(15);
-  const int stage = static_cast<int>(((dyn - pre) / waves_per_wg) & ~size_t(15));
   int share_bits = 0;
   if (!kVar && a.num_seqs > 1) {
     int bits = 1;
     while ((1 << bits) < 2 * a.num_seqs) ++bits;
     const size_t first = (sizeof(int) * static_cast<size_t>(a.num_seqs) + 15) & ~size_t(15);
-    if (first + (static_cast<size_t>(kShareSlotBytes) << bits) + (sizeof(int) << bits) <=
-        dyn - pre)
+    if (2 * pre + first + (static_cast<size_t>(kShareSlotBytes) << bits) +
+            (sizeof(int) << bits) <= dyn)
       share_bits = bits;
   }
+  const size_t pre_all = share_bits > 0 ? 2 * pre : pre;
+  const int stage = static_cast<int>(((dyn - pre_all) / waves_per_wg) & ~size_t(15));
   // whole groups of num_kv_heads waves, no more than the GPU holds at once
   int64_t waves = static_cast<int64_t>(sh.cus) * waves_per_wg;
   int64_t per_kv = waves / a.num_kv_heads;
