@@ -548,14 +548,16 @@ def test_merged_edge_lengths(dev, pkv):
         assert int(counters.abs().sum()) == 0
 
 
-def test_shared_prefix_groups(dev, pkv):
+@pytest.mark.parametrize("B", [16, 32])
+def test_shared_prefix_groups(dev, pkv, B):
     """Several groups of sequences sharing leading blocks (runs of 1 to 6
     blocks, a group whose members diverge after the first block, a member
     shorter than the run, single sequences): the split kernel finds them by
-    their first block and reads the shared lines ahead; the output equals
-    the oracle's, split and unsplit, merged in one launch or two."""
-    rng = np.random.default_rng(77)
-    B, N = 16, 400
+    their first block, reads the shared lines ahead and weighs shared tiles
+    less in its split; the output equals the oracle's, split and unsplit,
+    merged in one launch or two, down to two pieces per sequence."""
+    rng = np.random.default_rng(77 + B)
+    N = 400
     free = [int(x) for x in rng.permutation(N)]
     rows, lens = [], []
 
@@ -588,13 +590,16 @@ def test_shared_prefix_groups(dev, pkv):
                 head_size=128, block_size=B, num_blocks=N, block_table=table,
                 context_lens=np.array(lens, np.int32), free_order=np.arange(N, dtype=np.int32),
                 seed=4244)
-    say(f"case: shared prefix groups S={b.num_seqs}")
+    say(f"case: shared prefix groups S={b.num_seqs} B={B}")
     t = W.layer_tensors(b, device=dev)
     th = host(t)
     want = oracle_attention(b, th["q"], th["k_cache"], th["v_cache"])
     meta = device_meta(b, dev)
     counters = torch.zeros(b.num_seqs * b.num_kv_heads, dtype=torch.int32, device=dev)
-    for P in (0, 16, 64):
+    # (partitions are whole blocks; the last split leaves at most two pieces
+    # per sequence)
+    half = -(-int(max(lens)) // 2)
+    for P in (0, B, 4 * B, -(-half // B) * B):
         got = gpu_attention(pkv, b, t, meta, dev, P)
         torch.cuda.synchronize()
         e = max_err(got.cpu(), want)
