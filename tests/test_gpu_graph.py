@@ -137,3 +137,75 @@ def test_append_step_graph_replays_equal_eager(dev, pkv):
         for l, (o, want) in enumerate(zip(outs, eager)):
             assert torch.equal(o, want), (r, l)
         print(f"  replay {r}: equal to eager", flush=True)
+
+
+# A fresh process whose first call into the library is made under graph
+# capture: the library's per-device launch set-up (occupancy and LDS queries,
+# kernel attributes) then runs while the stream is capturing. Its replays
+# must equal the same call made eagerly afterwards, bit for bit, and the
+# oracle within 2e-3.
+_FIRST_CALL_UNDER_CAPTURE = r"""
+import sys, torch
+sys.path[:0] = [ROOT, ROOT + "/tests"]
+import paged_kv_cache_113_amd as pkv
+import workloads as W
+from gpu_cases import TOL, device_meta, host, max_err, oracle_attention, oracle_pools_after_write, scale_of
+dev = torch.device("cuda:0")
+b = W.decode_step_bf16(num_seqs=40, lo=1, hi=700, num_layers=1)
+t = W.layer_tensors(b, layer=0, device=dev)
+th = host(t)
+meta = device_meta(b, dev)
+P = 256
+mp = b.max_partitions(P)
+S, H, D = b.num_seqs, b.num_heads, b.head_size
+out = torch.empty(S, H, D, device=dev)
+ml = torch.empty(S, H, mp, device=dev)
+es = torch.empty_like(ml)
+to = torch.empty(S, H, mp, D, device=dev)
+counters = torch.zeros(S * b.num_kv_heads, dtype=torch.int32, device=dev)
+def call():
+    pkv.paged_decode_attention_append(out, t["q"], t["k_cache"], t["v_cache"], t["k_new"],
+                                      t["v_new"], meta["table"], meta["ctx"], scale_of(b), P, mp,
+                                      ml, es, to, counters)
+torch.cuda.synchronize()
+side = torch.cuda.Stream()
+side.wait_stream(torch.cuda.current_stream())
+g = torch.cuda.CUDAGraph()
+with torch.cuda.stream(side):
+    with torch.cuda.graph(g, stream=side):
+        call()                  # the process's first library call
+torch.cuda.current_stream().wait_stream(side)
+replays = []
+for _ in range(3):
+    out.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    replays.append(out.clone())
+    assert int(counters.abs().sum()) == 0
+out.fill_(float("nan"))
+call()
+torch.cuda.synchronize()
+eager = out.clone()
+for r in replays:
+    assert torch.equal(r.view(torch.int32), eager.view(torch.int32))
+k, v, _ = oracle_pools_after_write(b, th)
+want = oracle_attention(b, th["q"], k, v)
+e = max_err(eager.cpu(), want)
+assert e <= TOL, e
+print("first call under capture ok, max abs err %.3e" % e, flush=True)
+"""
+
+
+def test_first_call_under_capture():
+    import os
+    import subprocess
+    import sys
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    print("case: first library call of a fresh process made under graph capture", flush=True)
+    r = subprocess.run([sys.executable, "-c", f"ROOT = {root!r}\n" + _FIRST_CALL_UNDER_CAPTURE],
+                       capture_output=True, text=True, timeout=100)
+    print(r.stdout[-2000:], r.stderr[-3000:], flush=True)
+    assert r.returncode == 0
+    assert "first call under capture ok" in r.stdout
