@@ -30,10 +30,12 @@
  *
  * Ownership and threading: the caller allocates and owns every buffer. The
  * library allocates nothing and keeps no pointer after a call returns. Its
- * global state is a write-once, per-device cache of one occupancy query and
- * of the static scratch buffer's address (atomics; calls are reentrant and
- * thread-safe), and that buffer itself, which only
- * paged_varlen_attention_noalloc uses. It never synchronises:
+ * global state is a write-once, per-device cache of the launch shapes (CU
+ * count, LDS budget, occupancy; filled on a device's first call, which also
+ * sets the kernels' dynamic-LDS attribute, and valid when that first call is
+ * made under graph capture) and of the static scratch buffer's address
+ * (atomics; calls are reentrant and thread-safe), and that buffer itself,
+ * which only paged_varlen_attention_noalloc uses. It never synchronises:
  * each call validates its arguments on the host, then enqueues kernels on
  * `stream` (a hipStream_t passed as void*; NULL is the default stream) and
  * returns. Device faults surface at the caller's next synchronisation.
