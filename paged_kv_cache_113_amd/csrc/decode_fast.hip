@@ -408,7 +408,7 @@ __device__ __forceinline__ void merge_arrivals(const DecodeArgs& a, const int* s
 // holder have in common. Before the stream starts, the workgroups of each
 // XCD read every line of those runs once with plain loads, so that the lines
 // sit in that XCD's cache when the sharers' non-temporal stream reaches them.
-constexpr int kShareSlotBytes = 16;   // hash slot: key / run, lowest holder, count, another
+constexpr int kShareSlotBytes = 16;   // hash slot: key, lowest holder, count / run, highest
 __device__ __forceinline__ uint32_t share_hash(int32_t b, int bits) {
   return (static_cast<uint32_t>(b) * 2654435761u) >> (32 - bits);
 }
@@ -1164,8 +1164,8 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   // When this range starts with a sequence's last tile, every store comes
   // before the first tile's loads. Otherwise the first four tokens' rows are
   // loaded before the tile (so waiting for them does not wait for it), the
-  // tile's loads go out, then their stores; the rest follow the shared-block
-  // detection.
+  // tile's loads go out, then their stores; the rest follow the barrier
+  // that ends the shared-run work.
   const bool append = !kVar && a.k_new != nullptr && active;
   const bool first_is_new = append && pre(cur.s + 1) - 1 == b0;
   if (first_is_new) append_rest(0);
