@@ -1062,11 +1062,19 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     piece = 0;
   };
 
-  // Two register sets, unrolled by two; the q of the next unit is loaded
-  // before that unit's first tile, ahead of the tile loads, so a wait for a
-  // tile also covers it. Each processed tile has exactly one tile of loads
-  // behind it, or none, on every path.
-  TileRegs ta, tb;
+  // Tiles in flight while a tile is computed: one for decode, two for
+  // multi-token queries, whose tiles carry more softmax work per byte
+  // (speculative verify 1-3 % faster with two; decode and MHA 0.3-4 %
+  // slower, A-B runs on one box). kAhead + 1 register sets, unrolled by
+  // kAhead + 1. The q of a unit is loaded one step before the unit's first
+  // tile is computed, ahead of the loads issued in that step. On every path
+  // a processed tile has exactly kAhead tiles of loads behind it (fewer only
+  // at the end of the range). With one ahead the compiler's wait before a
+  // tile is for that tile alone; with two it also covers the first loads of
+  // the next tile (its count does not carry the previous step's loads across
+  // the loop), which leaves somewhat less than two tiles in flight.
+  constexpr int kAhead = kVar ? 2 : 1;
+  TileRegs ta, tb, tc;
   // Decode step: the new token of each sequence whose last tile lies in this
   // range goes into the pool here, for this wave's KV head, by the wave that
   // reads that tile (the only reader of that row in this launch): its later
@@ -1201,19 +1209,29 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   if (early && (__builtin_popcountll(m_new) > 4 || (lo + 64 < S && pre(lo + 64) < b1)))
     append_rest(4);
   if (!active) return;
-  bool gb = true;
-  Cursor nx = cur;
+  Cursor nx = cur;   // the tile after `cur`, once loaded
+  Cursor nx2 = cur;  // (two ahead) the newest tile loaded
+  bool gb = true, gc = true;
+  if constexpr (kAhead == 2) {
+    // the second tile, after the new tokens' stores (it may hold one); a
+    // one-tile range loads its only tile again (no branch: see above)
+    nx = len > 1 ? advance(cur) : cur;
+    gb = geo.load(tb, row_of(nx.s), nx.t * kTile, kvh);
+    nx2 = nx;
+  }
   int i = 0;
   auto step = [&](TileRegs& now, bool g_now, TileRegs& next, bool& g_next) {
-    // now = tile i (cur), next <- tile i + 1
+    // now = tile i (cur); next <- tile i + kAhead (with kAhead = 2, tile
+    // i + 1 (nx) is already in flight)
     const bool more = i + 1 < len;
+    if constexpr (kAhead == 1) nx = more ? advance(cur) : cur;
     const bool switch_unit = more && (cur.t + 1 >= cur.n);
     int slim, vlim;
     limits(cur, g_now, slim, vlim);
-    if (more) {
-      nx = advance(cur);
-      if (switch_unit) load_q_unit(qn, nx);
-      g_next = geo.load(next, row_of(nx.s), nx.t * kTile, kvh);
+    if (switch_unit) load_q_unit(qn, nx);
+    if (i + kAhead < len) {
+      nx2 = kAhead == 1 ? nx : advance(nx);
+      g_next = geo.load(next, row_of(nx2.s), nx2.t * kTile, kvh);
       issue_fence();
       st.tile(now, q, slim, vlim, qk_scale, grp, col, slot);
     } else {
@@ -1225,12 +1243,21 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
       for (int kk = 0; kk < 4; ++kk) q[kk] = qn[kk];
     }
     cur = nx;
+    nx = nx2;
     ++i;
     return more;
   };
-  while (true) {
-    if (!step(ta, ga, tb, gb)) break;
-    if (!step(tb, gb, ta, ga)) break;
+  if constexpr (kAhead == 1) {
+    while (true) {
+      if (!step(ta, ga, tb, gb)) break;
+      if (!step(tb, gb, ta, ga)) break;
+    }
+  } else {
+    while (true) {
+      if (!step(ta, ga, tc, gc)) break;
+      if (!step(tb, gb, ta, ga)) break;
+      if (!step(tc, gc, tb, gb)) break;
+    }
   }
   flush();
   // pieces of sequence s (per lane; t0, t1: its stream tiles)
