@@ -1019,7 +1019,8 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
 #pragma unroll
         for (int db = 0; db < 8; ++db) *(PKV_LDS f32x4*)(ob + db * 64) = st.acc[db] * inv;
         if (grp == 0)  // natural-log units
-          *(PKV_LDS f32x2*)(rec + 16 + nl * (kD * 4) + col * 8) = f32x2{st.m_run * kLn2, l_col};
+          *(PKV_LDS f32x2*)(rec + 16 + nl * (kD * 4) + col * 8) =
+              f32x2{st.m_max * kLn2, st.sum_at_max(l_col)};
       }
       if (lane == 0)
         *(PKV_LDS u32x4*)(rec) = u32x4{static_cast<unsigned>(sq), static_cast<unsigned>(cg),
@@ -1048,11 +1049,11 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
           if (single) {
             if (kVar) store_untracked(a.exp_sums + e, -1.f);
           } else if (fused) {
-            store_untracked_device(a.max_logits + e, st.m_run * kLn2);
-            store_untracked_device(a.exp_sums + e, l_col);
+            store_untracked_device(a.max_logits + e, st.m_max * kLn2);
+            store_untracked_device(a.exp_sums + e, st.sum_at_max(l_col));
           } else {
-            store_untracked(a.max_logits + e, st.m_run * kLn2);
-            store_untracked(a.exp_sums + e, l_col);
+            store_untracked(a.max_logits + e, st.m_max * kLn2);
+            store_untracked(a.exp_sums + e, st.sum_at_max(l_col));
           }
         }
       }

@@ -105,20 +105,37 @@ struct TileRegs {
 // current tile: the loads must be in flight while this tile is computed.
 __device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// A column's reference max (log2 units) moves only when a score exceeds it
+// by more than this: the probabilities then stay below 2^8, and the
+// accumulators are rescaled only on such a move (a few tiles per piece)
+// instead of on every tile. Sums and outputs are taken against the same
+// reference, so the partial stays exact.
+constexpr float kLazyRef = 8.f;
+
 // Running softmax state of one wave: lane (col n, group j) keeps column n's
-// running max and its partial sum over rows 4j..4j+3, and acc[db][r] =
-// O^T[16*db + 4j + r][n] (unnormalised), for 16 query columns.
+// reference max (m_run, see kLazyRef), its running max (m_max) and its
+// partial sum over rows 4j..4j+3 against the reference, and acc[db][r] =
+// O^T[16*db + 4j + r][n] (unnormalised, same reference), for 16 query
+// columns.
 template <typename T>
 struct Attend {
   float m_run;
+  float m_max;
   float l_part;
   f32x4 acc[8];
 
   __device__ __forceinline__ void reset() {
     m_run = -INFINITY;
+    m_max = -INFINITY;
     l_part = 0.f;
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // The column's partial sum against its running max (the max itself):
+  // l_ref 2^(m_run - m_max); 0 for a column with no position.
+  __device__ __forceinline__ float sum_at_max(float l_ref) const {
+    return m_max == -INFINITY ? 0.f : l_ref * fast_exp2(m_run - m_max);
   }
 
   // S^T tile = K_tile . Q^T: lane (col n, group j), register i -> position 4j + i.
@@ -131,19 +148,23 @@ struct Attend {
 
   // Online softmax over one tile: rows >= slim get no weight in this lane's
   // column (slim may differ from column to column: a causal limit per query
-  // token). Returns the tile's probabilities and the factor that rescales
-  // the running sums.
+  // token). Returns the tile's probabilities, the factor that rescales the
+  // running sums, and (wave-uniform) whether any column's reference moved.
   __device__ __forceinline__ float softmax(const f32x4& S, int slim, float qk_scale, int grp,
-                                           float* p) {
+                                           float* p, bool& moved) {
     float s[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] = (4 * grp + i < slim) ? S[i] * qk_scale : -INFINITY;
     float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mt = max_xor32(max_xor16(mt));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
+    m_max = fmaxf(m_max, mt);
+    // (from -inf any finite max moves the reference)
+    const bool move = mt > m_run + kLazyRef;
+    const float m_ref = move ? mt : m_run;
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    const float alpha = move ? fast_exp2(m_run - m_use) : 1.f;
+    m_run = m_ref;
+    moved = __any(move);
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - m_use);
     l_part = l_part * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
@@ -164,13 +185,16 @@ struct Attend {
     }
   }
 
-  // acc = alpha * acc + V^T . P^T with V from an LDS slot.
-  __device__ __forceinline__ void pv(const float* p, float alpha, int grp, int col,
+  // acc = alpha * acc + V^T . P^T with V from an LDS slot (alpha is 1 in
+  // every lane unless `moved`).
+  __device__ __forceinline__ void pv(const float* p, float alpha, bool moved, int grp, int col,
                                      const PKV_LDS char* slot) {
     uint2 phi, plo;
     split_p<T>(p, phi, plo);
+    if (moved) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+      for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+    }
     // lane (d = col, group j): positions 4j..4j+3 of dim 16*db + d, gathered by
     // the transpose read from row 4j + col/4, bytes 32*db + 8*(col%4)
     const PKV_LDS char* rbase = slot + (4 * grp + (col >> 2)) * kSlotRow + (col & 3) * 8;
@@ -191,9 +215,10 @@ struct Attend {
                                        float qk_scale, int grp, int col, PKV_LDS char* slot) {
     const f32x4 S = scores(t.k, q);
     float p[4];
-    const float alpha = softmax(S, slim, qk_scale, grp, p);
+    bool moved;
+    const float alpha = softmax(S, slim, qk_scale, grp, p, moved);
     stage_v(t.v, vlim, grp, col, slot);
-    pv(p, alpha, grp, col, slot);
+    pv(p, alpha, moved, grp, col, slot);
   }
 
   // Column sum of l over the four row groups, in every lane.
