@@ -100,6 +100,7 @@ struct Geo {
     for (int i = 0; i < 4; ++i) t.v[i] = stream_load(vc + base + v_off + i * 256);
     return blk >= 0;
   }
+
 };
 
 // Q^T operand of (sequence seq, KV head kvh): lane (col n, group j) holds
@@ -152,10 +153,14 @@ __global__ __launch_bounds__(kWavesUnsplit * 64) void decode_whole_kernel(Decode
   st.reset();
   auto tok = [&](int ti) { return (w + NW * ti) * kTile; };
 
-  // The next tile's loads are in flight while this one is computed (two
-  // register sets, unrolled by two). Every processed tile has either exactly
-  // one tile of loads issued after it or none on every path, so the wait
-  // before it is exact.
+  // The next tile's loads are issued before this one is computed (two
+  // register sets, unrolled by two). The last pair loads nothing ahead, and
+  // the compiler's wait analysis, which also walks that path, waits for all
+  // loads at the top of each pair: one tile in flight per wave, which at
+  // this kernel's occupancy (several workgroups per CU) keeps HBM busy.
+  // Issuing loads on every path (the last one redundant) gives exact waits
+  // but measured about 5 % slower on 64 x 32-head MHA: the redundant tile
+  // costs more than the deeper pipeline gains.
   TileRegs ta, tb;
   bool ga = true, gb = true;
   if (my_n > 0) ga = geo.load(ta, row, tok(0), kvh);
@@ -1068,12 +1073,14 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   // (speculative verify 1-3 % faster with two; decode and MHA 0.3-4 %
   // slower, A-B runs on one box). kAhead + 1 register sets, unrolled by
   // kAhead + 1. The q of a unit is loaded one step before the unit's first
-  // tile is computed, ahead of the loads issued in that step. On every path
-  // a processed tile has exactly kAhead tiles of loads behind it (fewer only
-  // at the end of the range). With one ahead the compiler's wait before a
-  // tile is for that tile alone; with two it also covers the first loads of
-  // the next tile (its count does not carry the previous step's loads across
-  // the loop), which leaves somewhat less than two tiles in flight.
+  // tile is computed, ahead of the loads issued in that step. Every step
+  // issues a tile's loads, the last kAhead steps of a range the newest tile
+  // again (at most kAhead redundant tiles per wave, cache hits): with the
+  // loads behind a branch, the compiler's wait analysis also walks the path
+  // that skips both the loads and the compute, and waits for the whole
+  // previous tile before the next step's address arithmetic reuses its
+  // registers. Unconditional, every tile has exactly kAhead tiles of loads
+  // behind it and each wait is for that tile alone.
   constexpr int kAhead = kVar ? 2 : 1;
   TileRegs ta, tb, tc;
   // Decode step: the new token of each sequence whose last tile lies in this
@@ -1230,14 +1237,11 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     int slim, vlim;
     limits(cur, g_now, slim, vlim);
     if (switch_unit) load_q_unit(qn, nx);
-    if (i + kAhead < len) {
-      nx2 = kAhead == 1 ? nx : advance(nx);
-      g_next = geo.load(next, row_of(nx2.s), nx2.t * kTile, kvh);
-      issue_fence();
-      st.tile(now, q, slim, vlim, qk_scale, grp, col, slot);
-    } else {
-      st.tile(now, q, slim, vlim, qk_scale, grp, col, slot);
-    }
+    if constexpr (kAhead == 1) nx2 = nx;  // (cur itself at the end of the range)
+    else if (i + kAhead < len) nx2 = advance(nx);
+    g_next = geo.load(next, row_of(nx2.s), nx2.t * kTile, kvh);
+    issue_fence();
+    st.tile(now, q, slim, vlim, qk_scale, grp, col, slot);
     if (cur.t + 1 >= cur.n || !more) finish(cur);
     if (switch_unit) {
 #pragma unroll
