@@ -1070,8 +1070,8 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
 
   // Tiles in flight while a tile is computed: one for decode, two for
   // multi-token queries, whose tiles carry more softmax work per byte
-  // (speculative verify 1-3 % faster with two; decode and MHA 0.3-4 %
-  // slower, A-B runs on one box). kAhead + 1 register sets, unrolled by
+  // (speculative verify 1-3 % faster with two; decode, GQA and MHA no
+  // faster, the decode step 0.1 % slower, A-B runs on one box). kAhead + 1 register sets, unrolled by
   // kAhead + 1. The q of a unit is loaded one step before the unit's first
   // tile is computed, ahead of the loads issued in that step. Every step
   // issues a tile's loads, the last kAhead steps of a range the newest tile
