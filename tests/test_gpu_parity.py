@@ -616,6 +616,10 @@ def test_shared_prefix_groups(dev, pkv, B):
 APPEND = {
     "decode_step_small": lambda: W.decode_step_bf16(num_seqs=32, lo=1, hi=200, num_layers=1),
     "decode_step_short": lambda: W.decode_step_bf16(num_seqs=300, lo=1, hi=40, num_layers=1),
+    # ~5 and ~23 sequence ends per wave's range: the second prefetched round
+    # of new rows, and the tokens past the first eight over several windows
+    "decode_step_mid": lambda: W.decode_step_bf16(num_seqs=700, lo=1, hi=120, num_layers=1),
+    "decode_step_many": lambda: W.decode_step_bf16(num_seqs=3000, lo=1, hi=24, num_layers=1),
     "gqa8_f16_step": lambda: W._uniform_case("gqa8_step", "f16", 64, 8, 128, 32, 7, 1, 700, 83,
                                              new_token=True),
     "plain_f32_step": lambda: W._uniform_case("plain_step", "f32", 8, 2, 64, 8, 5, 1, 100, 84,
