@@ -403,6 +403,10 @@ MANY = {
     # directly
     "short_gqa16_s8192": lambda: W._uniform_case("short_gqa16", "f16", 32, 2, 128, 16, 8192, 1,
                                                  40, 92),
+    # one sequence past the split kernel's LDS prefix: the plain kernel's
+    # partitions, aligned to multiples of the partition size
+    "short_gqa4_s8193": lambda: W._uniform_case("short_gqa4", "bf16", 32, 8, 128, 16, 8193, 1,
+                                                40, 93),
 }
 
 
@@ -450,6 +454,7 @@ MERGED = {
     "plain_bf16_d96": (SMALL["plain_bf16_d96"], 8),
     "short_gqa4_s4000": (MANY["short_gqa4_s4000"], 16),
     "short_gqa16_s8192": (MANY["short_gqa16_s8192"], 16),
+    "short_gqa4_s8193": (MANY["short_gqa4_s8193"], 16),
     "full_mha_fp16": (W.mha_fp16, 256),
     "full_gqa_shared_bf16": (W.gqa_shared_bf16, 1024),
     "full_long_split_bf16": (W.long_split_bf16, 1024),
@@ -620,6 +625,9 @@ APPEND = {
     # of new rows, and the tokens past the first eight over several windows
     "decode_step_mid": lambda: W.decode_step_bf16(num_seqs=700, lo=1, hi=120, num_layers=1),
     "decode_step_many": lambda: W.decode_step_bf16(num_seqs=3000, lo=1, hi=24, num_layers=1),
+    # past the split kernel's sequence capacity: write, plain split kernel,
+    # merge as three launches
+    "decode_step_s8193": lambda: W.decode_step_bf16(num_seqs=8193, lo=1, hi=24, num_layers=1),
     "gqa8_f16_step": lambda: W._uniform_case("gqa8_step", "f16", 64, 8, 128, 32, 7, 1, 700, 83,
                                              new_token=True),
     "plain_f32_step": lambda: W._uniform_case("plain_step", "f32", 8, 2, 64, 8, 5, 1, 100, 84,
