@@ -209,3 +209,58 @@ def test_first_call_under_capture():
     print(r.stdout[-2000:], r.stderr[-3000:], flush=True)
     assert r.returncode == 0
     assert "first call under capture ok" in r.stdout
+
+
+def test_varlen_graph_replays_equal_eager(dev, pkv):
+    """A multi-token step (decode tokens, speculative rows and prefill chunks
+    in one batch: the split kernel, the prefill kernel and the merge) under
+    capture, both with a caller's workspace and through the entry point that
+    allocates nothing (partials in the library's static buffer): four
+    replays each, with eager work between them, bit-equal to the eager call,
+    which is within 2e-3 of the oracle."""
+    from gpu_cases import oracle_varlen
+    b = W.mixed_prefill_bf16(num_decode=60, num_prefill=2, chunk=300, hi=2000)
+    print(f"case: graph capture of a mixed multi-token call, S={b.num_seqs} T={b.num_tokens}",
+          flush=True)
+    t = W.layer_tensors(b, device=dev)
+    th = host(t)
+    meta = device_meta(b, dev)
+    qsl = torch.as_tensor(b.query_start_loc, device=dev)
+    T, H, D = b.num_tokens, b.num_heads, b.head_size
+    mp = 8
+    out = torch.empty(T, H, D, device=dev)
+    ml = torch.empty(T, H, mp, device=dev)
+    es = torch.empty_like(ml)
+    to = torch.empty(T, H, mp, D, device=dev)
+    calls = {
+        "workspace": lambda: pkv.paged_varlen_attention(
+            out, t["q"], t["k_cache"], t["v_cache"], meta["table"], qsl, meta["ctx"],
+            scale_of(b), mp, ml, es, to),
+        "no allocation": lambda: pkv.paged_varlen_attention_noalloc(
+            out, t["q"], t["k_cache"], t["v_cache"], meta["table"], qsl, meta["ctx"],
+            scale_of(b), mp),
+    }
+    want = oracle_varlen(b, th["q"], th["k_cache"], th["v_cache"])
+    for name, call in calls.items():
+        call()                  # eager (fills the library's per-device caches)
+        torch.cuda.synchronize()
+        eager = out.clone()
+        e = max_err(eager.cpu(), want)
+        print(f"  {name}: eager max abs err {e:.3e}", flush=True)
+        assert e <= TOL
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for r in range(4):
+            out.fill_(float("nan"))   # eager work between replays
+            ml.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"{name}: replay {r} differs from the eager call"
+        print(f"  {name}: 4 replays bit-equal to eager", flush=True)
