@@ -1080,7 +1080,9 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
   // that skips both the loads and the compute, and waits for the whole
   // previous tile before the next step's address arithmetic reuses its
   // registers. Unconditional, every tile has exactly kAhead tiles of loads
-  // behind it and each wait is for that tile alone.
+  // behind it, and the waits are for that tile alone (checked in the
+  // assembly; with two ahead, the first of the three unrolled steps still
+  // waits as if one were).
   constexpr int kAhead = kVar ? 2 : 1;
   TileRegs ta, tb, tc;
   // Decode step: the new token of each sequence whose last tile lies in this
