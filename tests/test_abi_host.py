@@ -378,3 +378,24 @@ def test_product_path_does_not_import_the_oracle():
                     text = open(os.path.join(dirpath, fn)).read()
                     assert "import oracle" not in text and "from oracle" not in text, fn
                     assert "attn_ref" not in text and "liboracle" not in text, fn
+
+
+def test_binding_without_the_library_fails_loudly(tmp_path):
+    """With libpagedkv.so absent, importing the binding raises ImportError:
+    no call falls back to PyTorch or the oracle."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "paged_kv_cache_113_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "paged_kv_cache_113_amd", "__init__.py"), pkg / "__init__.py")
+    code = ("import sys; sys.path.insert(0, sys.argv[1])\n"
+            "try:\n"
+            "    import paged_kv_cache_113_amd\n"
+            "except ImportError as e:\n"
+            "    print('ImportError', e); sys.exit(0)\n"
+            "sys.exit(1)\n")
+    r = subprocess.run([sys.executable, "-c", code, str(tmp_path)], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "no fallback" in r.stdout
